@@ -1,0 +1,101 @@
+"""Python binding of the GDLA attention core: argument marshalling only.
+
+Every step of the computation runs in the HIP kernels behind include/gdla.h;
+these functions check tensor metadata, pick the current HIP stream and call
+the C ABI through ctypes.  Tensors are torch bf16 tensors on a ROCm device.
+"""
+import ctypes
+import math
+
+import torch
+
+from . import _lib
+
+D_QK, D_V, GROUP = 192, 128, 4
+
+
+def _stream_ptr(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _check(t, name, shape, dtype=torch.bfloat16):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s (got %s)" % (name, dtype, t.dtype))
+    if t.device.type != "cuda":
+        raise ValueError("%s must be on a ROCm device (got %s)" % (name, t.device))
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s (got %s)" % (name, tuple(shape), tuple(t.shape)))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def prefill(q_signal, q_noise, k, v, lam, gate, window=0, scale=None, out=None):
+    """GDLA attention core over every position of a [B, T] batch.
+
+    q_signal [B,T,4*n_kv,192], q_noise [B,T,n_kv,192], k [B,T,n_kv,192],
+    v [B,T,n_kv,128], lam [B,T,4*n_kv], gate [B,T,4*n_kv,128], all bf16.
+    window 0 = full causal, W >= 1 = keys t-W+1..t.  Returns out
+    [B,T,4*n_kv,128] bf16, enqueued on the current stream.
+    """
+    B, T, n_kv, d_qk = k.shape
+    n_sig = n_kv * GROUP
+    _check(q_signal, "q_signal", (B, T, n_sig, D_QK))
+    _check(q_noise, "q_noise", (B, T, n_kv, D_QK))
+    _check(k, "k", (B, T, n_kv, D_QK))
+    _check(v, "v", (B, T, n_kv, D_V))
+    _check(lam, "lam", (B, T, n_sig))
+    _check(gate, "gate", (B, T, n_sig, D_V))
+    if out is None:
+        out = torch.empty((B, T, n_sig, D_V), dtype=torch.bfloat16, device=k.device)
+    _check(out, "out", (B, T, n_sig, D_V))
+    if scale is None:
+        scale = 1.0 / math.sqrt(D_QK)
+    lib = _lib.load()
+    _lib.check(lib.gdla_prefill(
+        q_signal.data_ptr(), q_noise.data_ptr(), k.data_ptr(), v.data_ptr(), lam.data_ptr(),
+        gate.data_ptr(), out.data_ptr(), B, T, n_kv, GROUP, D_QK, D_V, int(window),
+        float(scale), _stream_ptr(k.device)))
+    return out
+
+
+def decode_workspace_size(B, n_kv, max_seqlen_k, window=0):
+    return int(_lib.load().gdla_decode_workspace_size(B, n_kv, max_seqlen_k, int(window)))
+
+
+def decode(q_signal, q_noise, k_cache, v_cache, cu_seqlens, max_seqlen_k, lam, gate,
+           window=0, scale=None, out=None, workspace=None):
+    """GDLA attention core for one new token per sequence over a packed KV cache.
+
+    q_signal [B,4*n_kv,192], q_noise [B,n_kv,192], k_cache [total,n_kv,192],
+    v_cache [total,n_kv,128], cu_seqlens int32 [B+1] (device; lengths include
+    the new token), lam [B,4*n_kv], gate [B,4*n_kv,128].  Returns out
+    [B,4*n_kv,128] bf16.  The workspace (uint8 device tensor) is allocated
+    here if not given.
+    """
+    total, n_kv, _ = k_cache.shape
+    B = q_signal.shape[0]
+    n_sig = n_kv * GROUP
+    _check(q_signal, "q_signal", (B, n_sig, D_QK))
+    _check(q_noise, "q_noise", (B, n_kv, D_QK))
+    _check(k_cache, "k_cache", (total, n_kv, D_QK))
+    _check(v_cache, "v_cache", (total, n_kv, D_V))
+    _check(cu_seqlens, "cu_seqlens", (B + 1,), dtype=torch.int32)
+    _check(lam, "lam", (B, n_sig))
+    _check(gate, "gate", (B, n_sig, D_V))
+    if out is None:
+        out = torch.empty((B, n_sig, D_V), dtype=torch.bfloat16, device=k_cache.device)
+    _check(out, "out", (B, n_sig, D_V))
+    if scale is None:
+        scale = 1.0 / math.sqrt(D_QK)
+    need = decode_workspace_size(B, n_kv, max_seqlen_k, window) if B > 0 else 0
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=k_cache.device)
+    lib = _lib.load()
+    _lib.check(lib.gdla_decode(
+        q_signal.data_ptr(), q_noise.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+        cu_seqlens.data_ptr(), int(max_seqlen_k), lam.data_ptr(), gate.data_ptr(),
+        out.data_ptr(), workspace.data_ptr(), workspace.numel(), B, n_kv, GROUP, D_QK, D_V,
+        int(window), float(scale), _stream_ptr(k_cache.device)))
+    return out

@@ -1,0 +1,159 @@
+// gdla_api.hip -- the extern "C" entry points declared in include/gdla.h:
+// host-side argument checks (before any HIP call), then the kernel launches.
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+
+#include "gdla.h"
+#include "gdla_launch.h"
+
+namespace {
+
+thread_local char g_last_error[256] = "";
+
+int fail(int code, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+struct Range {
+    const char *name;
+    uintptr_t lo, hi;
+};
+
+bool overlaps(const Range &a, const Range &b) { return a.lo < b.hi && b.lo < a.hi; }
+
+int check_head_shape(int n_kv, int group, int d_qk, int d_v) {
+    if (n_kv < 1 || group < 1 || d_qk < 1 || d_v < 1)
+        return fail(GDLA_ERR_INVALID_ARG, "n_kv, group, d_qk, d_v must be >= 1 (got %d, %d, %d, %d)",
+                    n_kv, group, d_qk, d_v);
+    if (group != 4 || d_qk != 192 || d_v != 128)
+        return fail(GDLA_ERR_UNSUPPORTED,
+                    "this build implements group=4, d_qk=192, d_v=128 (got %d, %d, %d)", group, d_qk, d_v);
+    return GDLA_OK;
+}
+
+int check_scale_window(float scale, int window) {
+    if (!std::isfinite(scale) || !(scale > 0.f))
+        return fail(GDLA_ERR_INVALID_ARG, "softmax_scale must be finite and > 0 (got %g)", (double)scale);
+    if (window < 0) return fail(GDLA_ERR_INVALID_ARG, "window must be >= 0 (got %d)", window);
+    return GDLA_OK;
+}
+
+}  // namespace
+
+extern "C" int gdla_abi_version(void) { return 1; }
+
+extern "C" const char *gdla_status_string(int status) {
+    switch (status) {
+        case GDLA_OK: return "GDLA_OK";
+        case GDLA_ERR_INVALID_ARG: return "GDLA_ERR_INVALID_ARG: invalid argument";
+        case GDLA_ERR_UNSUPPORTED: return "GDLA_ERR_UNSUPPORTED: head shape not implemented";
+        case GDLA_ERR_MISALIGNED: return "GDLA_ERR_MISALIGNED: tensor pointer not 16-byte aligned";
+        case GDLA_ERR_WORKSPACE: return "GDLA_ERR_WORKSPACE: decode workspace missing or too small";
+        case GDLA_ERR_HIP: return "GDLA_ERR_HIP: HIP runtime error";
+        default: return "GDLA: unknown status";
+    }
+}
+
+extern "C" const char *gdla_last_error(void) { return g_last_error; }
+
+extern "C" int gdla_prefill(const void *q_signal, const void *q_noise, const void *k, const void *v,
+                            const void *lambda_, const void *gate, void *out, int B, int T, int n_kv,
+                            int group, int d_qk, int d_v, int window, float softmax_scale,
+                            void *stream) {
+    g_last_error[0] = 0;
+    if (B < 0 || T < 0) return fail(GDLA_ERR_INVALID_ARG, "B and T must be >= 0 (got %d, %d)", B, T);
+    if (int rc = check_head_shape(n_kv, group, d_qk, d_v)) return rc;
+    if (int rc = check_scale_window(softmax_scale, window)) return rc;
+    if (B == 0 || T == 0) return GDLA_OK;
+
+    const void *ptrs[7] = {q_signal, q_noise, k, v, lambda_, gate, out};
+    const char *names[7] = {"q_signal", "q_noise", "k", "v", "lambda", "gate", "out"};
+    for (int i = 0; i < 7; ++i) {
+        if (!ptrs[i]) return fail(GDLA_ERR_INVALID_ARG, "%s is NULL", names[i]);
+        if (!aligned(ptrs[i], 16)) return fail(GDLA_ERR_MISALIGNED, "%s is not 16-byte aligned", names[i]);
+    }
+    const long double rows = (long double)B * T;
+    const long double n_sig = (long double)n_kv * group;
+    if (rows * n_sig * d_qk * 2 >= 4.6e18L)
+        return fail(GDLA_ERR_INVALID_ARG, "tensor sizes exceed the 2^62-byte limit");
+    if (gdla::prefill_grid_blocks(B, T, n_kv) >= (1L << 31))
+        return fail(GDLA_ERR_INVALID_ARG, "B * n_kv * ceil(T/64) must be < 2^31");
+
+    const uintptr_t r = (uintptr_t)B * (uintptr_t)T;
+    const uintptr_t ns = (uintptr_t)n_kv * group;
+    const Range in[6] = {
+        {"q_signal", (uintptr_t)q_signal, (uintptr_t)q_signal + r * ns * d_qk * 2},
+        {"q_noise", (uintptr_t)q_noise, (uintptr_t)q_noise + r * n_kv * d_qk * 2},
+        {"k", (uintptr_t)k, (uintptr_t)k + r * n_kv * d_qk * 2},
+        {"v", (uintptr_t)v, (uintptr_t)v + r * n_kv * d_v * 2},
+        {"lambda", (uintptr_t)lambda_, (uintptr_t)lambda_ + r * ns * 2},
+        {"gate", (uintptr_t)gate, (uintptr_t)gate + r * ns * d_v * 2}};
+    const Range o = {"out", (uintptr_t)out, (uintptr_t)out + r * ns * d_v * 2};
+    for (const Range &x : in)
+        if (overlaps(o, x)) return fail(GDLA_ERR_INVALID_ARG, "out overlaps %s", x.name);
+
+    hipError_t e = gdla::launch_prefill(q_signal, q_noise, k, v, lambda_, gate, out, B, T, n_kv,
+                                        window, softmax_scale, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(GDLA_ERR_HIP, "prefill launch: %s", hipGetErrorString(e));
+    return GDLA_OK;
+}
+
+extern "C" size_t gdla_decode_workspace_size(int B, int n_kv, int max_seqlen_k, int window) {
+    if (B < 1 || n_kv < 1 || max_seqlen_k < 1 || window < 0) return 0;
+    return gdla::decode_workspace_bytes(B, n_kv, gdla::decode_splits(max_seqlen_k, window));
+}
+
+extern "C" int gdla_decode(const void *q_signal, const void *q_noise, const void *k_cache,
+                           const void *v_cache, const int32_t *cu_seqlens_k, int max_seqlen_k,
+                           const void *lambda_, const void *gate, void *out, void *workspace,
+                           size_t workspace_bytes, int B, int n_kv, int group, int d_qk, int d_v,
+                           int window, float softmax_scale, void *stream) {
+    g_last_error[0] = 0;
+    if (B < 0 || B > 65535) return fail(GDLA_ERR_INVALID_ARG, "B must be in [0, 65535] (got %d)", B);
+    if (int rc = check_head_shape(n_kv, group, d_qk, d_v)) return rc;
+    if (n_kv > 65535) return fail(GDLA_ERR_INVALID_ARG, "n_kv must be <= 65535 (got %d)", n_kv);
+    if (int rc = check_scale_window(softmax_scale, window)) return rc;
+    if (B == 0) return GDLA_OK;
+    if (max_seqlen_k < 1) return fail(GDLA_ERR_INVALID_ARG, "max_seqlen_k must be >= 1 (got %d)", max_seqlen_k);
+
+    const void *ptrs[7] = {q_signal, q_noise, k_cache, v_cache, lambda_, gate, out};
+    const char *names[7] = {"q_signal", "q_noise", "k_cache", "v_cache", "lambda", "gate", "out"};
+    for (int i = 0; i < 7; ++i) {
+        if (!ptrs[i]) return fail(GDLA_ERR_INVALID_ARG, "%s is NULL", names[i]);
+        if (!aligned(ptrs[i], 16)) return fail(GDLA_ERR_MISALIGNED, "%s is not 16-byte aligned", names[i]);
+    }
+    if (!cu_seqlens_k) return fail(GDLA_ERR_INVALID_ARG, "cu_seqlens_k is NULL");
+    if (!aligned(cu_seqlens_k, 4)) return fail(GDLA_ERR_MISALIGNED, "cu_seqlens_k is not 4-byte aligned");
+
+    const int n_split = gdla::decode_splits(max_seqlen_k, window);
+    const size_t need = gdla::decode_workspace_bytes(B, n_kv, n_split);
+    if (need > 0) {
+        if (!workspace) return fail(GDLA_ERR_WORKSPACE, "workspace is NULL, %zu bytes needed", need);
+        if (workspace_bytes < need)
+            return fail(GDLA_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
+        if (!aligned(workspace, 16)) return fail(GDLA_ERR_MISALIGNED, "workspace is not 16-byte aligned");
+    }
+    const uintptr_t ns = (uintptr_t)n_kv * group;
+    const Range o = {"out", (uintptr_t)out, (uintptr_t)out + (uintptr_t)B * ns * d_v * 2};
+    const Range in[4] = {
+        {"q_signal", (uintptr_t)q_signal, (uintptr_t)q_signal + (uintptr_t)B * ns * d_qk * 2},
+        {"q_noise", (uintptr_t)q_noise, (uintptr_t)q_noise + (uintptr_t)B * n_kv * d_qk * 2},
+        {"lambda", (uintptr_t)lambda_, (uintptr_t)lambda_ + (uintptr_t)B * ns * 2},
+        {"gate", (uintptr_t)gate, (uintptr_t)gate + (uintptr_t)B * ns * d_v * 2}};
+    for (const Range &x : in)
+        if (overlaps(o, x)) return fail(GDLA_ERR_INVALID_ARG, "out overlaps %s", x.name);
+
+    hipError_t e = gdla::launch_decode(q_signal, q_noise, k_cache, v_cache, cu_seqlens_k, lambda_,
+                                       gate, out, workspace, B, n_kv, n_split, window, softmax_scale,
+                                       static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(GDLA_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
+    return GDLA_OK;
+}

@@ -1,0 +1,27 @@
+// gdla_launch.h -- host-side launchers of the gfx950 kernels (internal to the
+// library; the public surface is include/gdla.h).  Arguments are assumed
+// validated by the caller.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gdla {
+
+hipError_t launch_prefill(const void *qs, const void *qn, const void *k, const void *v,
+                          const void *lam, const void *gate, void *out, int B, int T, int n_kv,
+                          int window, float scale, hipStream_t stream);
+long prefill_grid_blocks(int B, int T, int n_kv);
+
+// Number of cache splits (workgroups per (sequence, KV head)) for decode.
+int decode_splits(int max_seqlen_k, int window);
+// Workspace bytes for the split partials (0 when decode_splits() == 1).
+size_t decode_workspace_bytes(int B, int n_kv, int n_split);
+
+hipError_t launch_decode(const void *qs, const void *qn, const void *kc, const void *vc,
+                         const int32_t *cu_seqlens, const void *lam, const void *gate, void *out,
+                         void *workspace, int B, int n_kv, int n_split, int window, float scale,
+                         hipStream_t stream);
+
+}  // namespace gdla

@@ -1,0 +1,261 @@
+"""Benchmark of the GDLA attention core on one MI355X.
+
+One step = one pass of the fused prefill kernel over the full-causal workload
+(batch 1, T = 4096, 16 KV heads / 64 signal / 16 noise heads, qk 192 / v 128,
+bf16, synthetic seeded inputs already resident in HBM).  The kernel does the
+whole hot path: band limits, K/V tiles, QK^T, mask, softmax, PV, the
+differential combine and the gate.
+
+Printed: ONE JSON line with the throughput (unmasked FLOPs / time), the
+roofline of the prefill kernel (timed with HIP events on the stream it runs
+on), the CPU oracle timed on a bounded sample of the same workload, and the
+other workloads (sliding-window prefill, 128K prefill, decode) under "extra".
+
+    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--no-extra]
+"""
+import argparse
+import glob
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "GDLA prefill TFLOP/s + decode HBM GB/s, each as % of MI355X roofline"
+PEAK_BF16_TFLOPS = 2516.6      # 256 CU x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU
+PEAK_HBM_GBS = 8000.0
+FLOP_PER_PAIR = 640            # 2*192 (QK^T) + 2*128 (PV) per (query head, query, key)
+N_HEADS = 80                   # 64 signal + 16 noise query heads
+
+
+def pairs_prefill(B, T, window):
+    if window <= 0 or window >= T:
+        return B * T * (T + 1) // 2
+    return B * (window * (window + 1) // 2 + (T - window) * window)
+
+
+def prefill_bytes(B, T, n_kv=16, n_sig=64):
+    # q_signal, q_noise, k, v, lambda, gate in; out written; each once (bf16)
+    per_tok = 2 * (n_sig * 192 + n_kv * 192 + n_kv * 192 + n_kv * 128 + n_sig + 2 * n_sig * 128)
+    return B * T * per_tok
+
+
+def decode_bytes(lengths, window, n_kv=16, n_sig=64):
+    vis = [min(L, window) if window > 0 else L for L in lengths]
+    per_seq = 2 * (n_sig * 192 + n_kv * 192 + n_sig + 2 * n_sig * 128)
+    return sum(vis) * n_kv * (192 + 128) * 2 + len(lengths) * per_seq + 4 * (len(lengths) + 1)
+
+
+def source_hash():
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "attention_gdla_prefill_amd", "csrc", "*"))):
+        h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def time_kernel(fn, steps, warmup, stream):
+    """Run fn warmup+steps times; return (wall ms/step, per-launch HIP-event ms list)."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    t0 = time.perf_counter()
+    for a, b in ev:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    return wall, [a.elapsed_time(b) for a, b in ev]
+
+
+def cpu_baseline(budget_s=15.0):
+    """The oracle, untuned, on a random sample of query rows of the 4K workload."""
+    import numpy as np
+    import torch
+    import oracle
+    import workload as W
+    w = W.WORKLOADS["pf_full_4k"]
+    x = W.prefill_inputs(w, seed=0, device="cpu")
+    f = {k: v.float().numpy() for k, v in x.items()}
+    rng = np.random.default_rng(0)
+    n, done_rows, done_pairs, elapsed = 32, 0, 0, 0.0
+    while elapsed < budget_s:
+        rt = rng.integers(0, w.T, size=n).astype(np.int32)
+        rb = np.zeros(n, np.int32)
+        t0 = time.perf_counter()
+        oracle.prefill_rows(f["k"], f["v"], f["q_signal"][0, rt], f["q_noise"][0, rt], f["lam"][0, rt],
+                            f["gate"][0, rt], rb, rt, window=0)
+        elapsed += time.perf_counter() - t0
+        done_rows += n
+        done_pairs += int((rt.astype(np.int64) + 1).sum())
+        n *= 2
+    tflops = done_pairs * N_HEADS * FLOP_PER_PAIR / elapsed / 1e12
+    return {"value": tflops, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": "%d random query rows (all 80 heads) of the B=1 T=4096 full-causal prefill, "
+                      "%.1f s of CPU time, fp64 oracle" % (done_rows, elapsed)}
+
+
+def load_traffic(name):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they
+    were taken on the current kernel sources."""
+    p = os.path.join(ROOT, "profiles", "traffic_%s.json" % name)
+    if not os.path.exists(p):
+        return None
+    t = json.load(open(p))
+    if t.get("source_hash") != source_hash():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def bench_prefill(name, steps, warmup):
+    import torch
+    import attention_gdla_prefill_amd as gdla
+    import workload as W
+    w = W.WORKLOADS[name]
+    x = W.prefill_inputs(w, seed=0, device="cuda")
+    out = torch.empty((w.B, w.T, w.n_sig, 128), dtype=torch.bfloat16, device="cuda")
+    stream = torch.cuda.current_stream()
+    fn = lambda: gdla.prefill(x["q_signal"], x["q_noise"], x["k"], x["v"], x["lam"], x["gate"],
+                              window=w.window, out=out)
+    wall, ev = time_kernel(fn, steps, warmup, stream)
+    kern_ms = sum(ev) / len(ev)
+    flops = pairs_prefill(w.B, w.T, w.window) * N_HEADS * FLOP_PER_PAIR
+    nbytes = prefill_bytes(w.B, w.T)
+    del x, out
+    torch.cuda.empty_cache()
+    return {"wall_ms": wall, "kernel_ms": kern_ms, "flops": flops, "bytes": nbytes,
+            "tflops": flops / (kern_ms * 1e-3) / 1e12, "gbs": nbytes / (kern_ms * 1e-3) / 1e9}
+
+
+def bench_decode(name, steps, warmup):
+    import torch
+    import attention_gdla_prefill_amd as gdla
+    import workload as W
+    w = W.WORKLOADS[name]
+    d = W.decode_inputs(w, seed=0, device="cuda")
+    lengths = d["lengths"].tolist()
+    max_len = max(lengths)
+    out = torch.empty((w.B, w.n_sig, 128), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(max(16, gdla.decode_workspace_size(w.B, w.n_kv, max_len, w.window)),
+                     dtype=torch.uint8, device="cuda")
+    # a buffer larger than the 256 MB Infinity Cache, rewritten before each launch
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    call = lambda: gdla.decode(d["q_signal"], d["q_noise"], d["k_cache"], d["v_cache"],
+                               d["cu_seqlens"], max_len, d["lam"], d["gate"], window=w.window,
+                               out=out, workspace=ws)
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(steps):
+        flush.fill_(1)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        call()
+        b.record(stream)
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b))
+    kern_ms = sorted(times)[len(times) // 2]
+    nbytes = decode_bytes(lengths, w.window)
+    del d, out, ws, flush
+    torch.cuda.empty_cache()
+    return {"kernel_ms": kern_ms, "bytes": nbytes, "gbs": nbytes / (kern_ms * 1e-3) / 1e9,
+            "hbm_frac": nbytes / (kern_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+            "cache": "cold (512 MB buffer rewritten before each launch)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="pf_full_4k", choices=["pf_full_4k", "pf_swa_32k", "pf_full_128k"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run one 1 GiB device copy (reference for HBM counter scaling)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import workload as W
+    if not torch.cuda.is_available():
+        print("bench.py needs a ROCm GPU", file=sys.stderr)
+        sys.exit(1)
+    import attention_gdla_prefill_amd._lib as L
+    L.load()          # fails loudly if the HIP library is missing
+
+    w = W.WORKLOADS[args.workload]
+    print("[bench] %s steps=%d warmup=%d" % (args.workload, args.steps, args.warmup),
+          file=sys.stderr, flush=True)
+    main_res = bench_prefill(args.workload, args.steps, args.warmup)
+
+    if args.copy_probe:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    extra = {}
+    if not args.no_extra:
+        for name in ("pf_swa_32k", "pf_full_128k"):
+            if name == args.workload:
+                continue
+            print("[bench] extra %s" % name, file=sys.stderr, flush=True)
+            steps = 3 if name == "pf_full_128k" else 10
+            r = bench_prefill(name, steps, 1)
+            extra[name] = {"tflops": r["tflops"], "mfma_frac": r["tflops"] / PEAK_BF16_TFLOPS,
+                           "gbs": r["gbs"], "hbm_frac": r["gbs"] / PEAK_HBM_GBS,
+                           "kernel_ms": r["kernel_ms"], "steps": steps}
+        for name in ("dec_full", "dec_swa"):
+            print("[bench] extra %s" % name, file=sys.stderr, flush=True)
+            extra[name] = bench_decode(name, 10, 2)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline", file=sys.stderr, flush=True)
+        cpu = cpu_baseline()
+
+    traffic = load_traffic(args.workload)
+    line = {
+        "metric": METRIC,
+        "value": main_res["flops"] / (main_res["wall_ms"] * 1e-3) / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": main_res["wall_ms"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "%s: prefill B=%d T=%d, %d KV / %d signal / %d noise heads, qk 192 / "
+                               "v 128, %s" % (w.name, w.B, w.T, w.n_kv, w.n_sig, w.n_kv,
+                                              "full causal" if w.window == 0 else "window %d" % w.window),
+                   "global_batch": w.B, "seq_len": w.T, "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "achieved": main_res["tflops"], "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": main_res["tflops"] / PEAK_BF16_TFLOPS,
+                     "traffic": traffic, "kernel": "prefill_kernel",
+                     "kernel_ms": main_res["kernel_ms"], "flops_per_launch": main_res["flops"],
+                     "algorithmic_bytes_per_launch": main_res["bytes"]},
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

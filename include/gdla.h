@@ -1,0 +1,143 @@
+/*
+ * gdla.h -- C ABI of the GDLA attention core on AMD Instinct MI355X (gfx950).
+ *
+ * Grouped Differential Latent Attention (GDLA), as the Motif 3 technical
+ * report describes it (aitrends.kr, "314B MoE 언어 모델 Motif 3의 구조와 학습
+ * 시스템", GDLA and grouped-differential paragraphs; shapes from metalmedia,
+ * Table 1): every KV head j serves one group of `group` = 4 signal query heads
+ * (4j .. 4j+3) and one noise query head (j).  Both paths share the KV head's
+ * K (query-key dim 192) and V (value dim 128), and each query head runs causal
+ * softmax attention over it -- full causal, or a sliding window of W keys
+ * (the report's hybrid layers use W = 128; aitrends.kr context-parallel
+ * paragraph, idailynews).  The library then forms
+ *     D[t,h,:] = H_S[t,h,:] - lambda[t,h] * H_N[t, h/4, :]
+ * (the noise output repeated to the 4 signal heads of its group) and applies
+ * the element-wise output gate,
+ *     out[t,h,:] = gate[t,h,:] * D[t,h,:].
+ * The output projection that follows in the model is not part of this
+ * library.  With a window W >= 1 a query at position t sees keys
+ * max(0, t-W+1) .. t; with W = 0 it sees 0 .. t.
+ *
+ * Conventions shared by every entry point:
+ *   - Every tensor pointer is a DEVICE pointer to a dense, row-major array
+ *     (last dimension fastest) of bf16 values, unless stated otherwise, and
+ *     must be 16-byte aligned.  The caller owns all memory; the library
+ *     allocates nothing, keeps no pointer after the call returns, and holds no
+ *     mutable global state besides a per-thread error-detail string.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Work is enqueued on it and the call returns without waiting; the caller
+ *     synchronises before reading `out`.
+ *   - Arguments are checked on the host before any HIP call.  A rejected call
+ *     returns a nonzero status, launches nothing and leaves `out` untouched.
+ *     gdla_last_error() gives a one-line reason for the last nonzero status
+ *     returned on the calling thread.
+ *   - Values are used as given: lambda is not clamped and the scale is not
+ *     altered.  Arithmetic: bf16 products accumulated in fp32, softmax in
+ *     fp32, the combine and gate in fp32, one rounding to bf16 (nearest-even)
+ *     on the final store.
+ *   - This build supports group = 4, d_qk = 192, d_v = 128 and any
+ *     n_kv >= 1; other head shapes return GDLA_ERR_UNSUPPORTED.
+ */
+#ifndef GDLA_H
+#define GDLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes returned (as int) by every entry point. */
+enum gdla_status {
+    GDLA_OK = 0,
+    GDLA_ERR_INVALID_ARG = 1,   /* null pointer, negative size, non-finite scale, ...   */
+    GDLA_ERR_UNSUPPORTED = 2,   /* head shape outside what this build implements       */
+    GDLA_ERR_MISALIGNED = 3,    /* a tensor pointer is not 16-byte aligned             */
+    GDLA_ERR_WORKSPACE = 4,     /* decode workspace missing or smaller than required   */
+    GDLA_ERR_HIP = 5            /* the HIP runtime reported an error at launch         */
+};
+
+/* Version of this ABI (incremented on any incompatible change). */
+int gdla_abi_version(void);
+
+/* Static, human-readable name of a status code. */
+const char *gdla_status_string(int status);
+
+/* Reason for the last nonzero status returned on this thread ("" if none). */
+const char *gdla_last_error(void);
+
+/*
+ * gdla_prefill -- attention core for every position of B sequences of T
+ * tokens (prefill / training-forward shape).
+ *
+ *   q_signal [B, T, n_kv*group, d_qk]  signal queries (post-RoPE); head h reads KV head h/group
+ *   q_noise  [B, T, n_kv, d_qk]        noise queries; head j reads KV head j
+ *   k        [B, T, n_kv, d_qk]        keys (post-RoPE)
+ *   v        [B, T, n_kv, d_v]         values
+ *   lambda_  [B, T, n_kv*group]        one coefficient per (token, signal head)
+ *   gate     [B, T, n_kv*group, d_v]   output gate, already through its sigmoid
+ *   out      [B, T, n_kv*group, d_v]   result; every element is written; must
+ *                                      not overlap any input
+ *   window        0 = full causal, W >= 1 = sliding window of W keys
+ *   softmax_scale multiplies q.k before the softmax (callers usually pass
+ *                 1/sqrt(d_qk)); must be finite
+ *
+ * B = 0 or T = 0 is a valid empty call: GDLA_OK, nothing launched.
+ * Limits: B*T*n_kv*group*d_v < 2^62; B*n_kv*ceil(T/64) < 2^31.
+ */
+int gdla_prefill(const void *q_signal, const void *q_noise, const void *k, const void *v,
+                 const void *lambda_, const void *gate, void *out,
+                 int B, int T, int n_kv, int group, int d_qk, int d_v,
+                 int window, float softmax_scale, void *stream);
+
+/*
+ * gdla_decode_workspace_size -- bytes of device workspace gdla_decode needs
+ * for B sequences, n_kv KV heads, cached lengths up to max_seqlen_k and the
+ * given window.  0 means no workspace is needed (a single pass suffices).
+ * Returns 0 as well for invalid arguments (gdla_decode then rejects them).
+ */
+size_t gdla_decode_workspace_size(int B, int n_kv, int max_seqlen_k, int window);
+
+/*
+ * gdla_decode -- attention core for one new token per sequence over a packed
+ * KV cache (autoregressive decode).  The cache holds the expanded per-head
+ * K and V; the report's KV path expands the compressed KV into 16 KV heads
+ * and shares one KV state between the signal and noise paths (aitrends.kr,
+ * GDLA paragraph; metalmedia, Table 1).
+ *
+ *   q_signal     [B, n_kv*group, d_qk]
+ *   q_noise      [B, n_kv, d_qk]
+ *   k_cache      [total_k, n_kv, d_qk]   sequence b owns rows cu[b] .. cu[b+1]-1
+ *   v_cache      [total_k, n_kv, d_v]
+ *   cu_seqlens_k DEVICE int32 [B+1], nondecreasing, 4-byte aligned.  The
+ *                length L_b = cu[b+1]-cu[b] already includes the new token
+ *                (the caller appends its K/V first); the query sits at
+ *                position L_b-1 and sees keys max(0, L_b-W) .. L_b-1.  A
+ *                sequence with L_b <= 0 gets an all-zero output row.
+ *   max_seqlen_k host-side upper bound on L_b; it sizes the split of the
+ *                cache across workgroups (any L_b is still computed
+ *                correctly, only less evenly split, if it is exceeded)
+ *   lambda_      [B, n_kv*group]
+ *   gate         [B, n_kv*group, d_v]
+ *   out          [B, n_kv*group, d_v]   every element written; no overlap with inputs
+ *   workspace    device scratch of at least
+ *                gdla_decode_workspace_size(B, n_kv, max_seqlen_k, window)
+ *                bytes (may be NULL when that size is 0); contents on entry
+ *                are ignored; calls sharing one workspace must be ordered on
+ *                one stream
+ *
+ * B = 0 is a valid empty call.
+ */
+int gdla_decode(const void *q_signal, const void *q_noise, const void *k_cache,
+                const void *v_cache, const int32_t *cu_seqlens_k, int max_seqlen_k,
+                const void *lambda_, const void *gate, void *out,
+                void *workspace, size_t workspace_bytes,
+                int B, int n_kv, int group, int d_qk, int d_v,
+                int window, float softmax_scale, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDLA_H */

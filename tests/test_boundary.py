@@ -1,0 +1,127 @@
+"""CPU tests of the C ABI boundary (no GPU needed, no kernel is launched).
+
+Every argument check in libgdla.so runs on the host before any HIP call, so
+rejected calls can be exercised here with fake pointer values.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from attention_gdla_prefill_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdla.h")
+
+OK, INVALID, UNSUPPORTED, MISALIGNED, WORKSPACE, HIP = range(6)
+A = 0x10000          # a fake, 16-byte aligned "device" address (never dereferenced)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIBRARY):
+        from attention_gdla_prefill_amd import build
+        build.build_library(quiet=True)
+    return _lib.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdla_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert {"gdla_prefill", "gdla_decode", "gdla_decode_workspace_size"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(_lib.SIGNATURES), "binding and header disagree"
+
+
+def test_status_strings(lib):
+    assert lib.gdla_abi_version() == 1
+    for s in range(6):
+        assert lib.gdla_status_string(s).decode().startswith("GDLA_")
+    assert b"unknown" in lib.gdla_status_string(99)
+
+
+def prefill(lib, ptrs=None, B=1, T=64, n_kv=16, group=4, d_qk=192, d_v=128, window=0, scale=0.07):
+    if ptrs is None:
+        ptrs = [A + i * (1 << 32) for i in range(7)]
+    return lib.gdla_prefill(*ptrs, B, T, n_kv, group, d_qk, d_v, window, ctypes.c_float(scale), None)
+
+
+def test_prefill_rejections(lib):
+    assert prefill(lib, B=-1) == INVALID
+    assert prefill(lib, T=-3) == INVALID
+    assert prefill(lib, n_kv=0) == INVALID
+    assert prefill(lib, group=5) == UNSUPPORTED
+    assert prefill(lib, d_qk=128) == UNSUPPORTED
+    assert prefill(lib, d_v=64) == UNSUPPORTED
+    assert prefill(lib, window=-1) == INVALID
+    assert prefill(lib, scale=float("nan")) == INVALID
+    assert prefill(lib, scale=float("inf")) == INVALID
+    assert prefill(lib, scale=0.0) == INVALID
+    for i in range(7):
+        ptrs = [A + k * (1 << 32) for k in range(7)]
+        ptrs[i] = None
+        assert prefill(lib, ptrs) == INVALID
+        assert lib.gdla_last_error() != b""
+        ptrs[i] = A + 8 + i * (1 << 32)
+        assert prefill(lib, ptrs) == MISALIGNED
+    # out overlapping an input
+    ptrs = [A + k * (1 << 32) for k in range(7)]
+    ptrs[6] = ptrs[5] + 4096
+    assert prefill(lib, ptrs) == INVALID
+    assert b"overlaps" in lib.gdla_last_error()
+    # grid limit
+    assert prefill(lib, B=40000, T=1 << 20, n_kv=16) == INVALID
+
+
+def test_prefill_empty_is_noop(lib):
+    assert prefill(lib, [None] * 7, B=0) == OK
+    assert prefill(lib, [None] * 7, T=0) == OK
+
+
+def decode(lib, ptrs=None, cu=A + 0x700000000, max_len=4096, ws=None, ws_bytes=0, B=2, n_kv=16,
+           group=4, d_qk=192, d_v=128, window=0, scale=0.07):
+    if ptrs is None:
+        ptrs = [A + i * (1 << 32) for i in range(7)]
+    qs, qn, kc, vc, lam, gate, out = ptrs
+    return lib.gdla_decode(qs, qn, kc, vc, cu, max_len, lam, gate, out, ws, ws_bytes, B, n_kv,
+                           group, d_qk, d_v, window, ctypes.c_float(scale), None)
+
+
+def test_decode_workspace_size(lib):
+    assert lib.gdla_decode_workspace_size(64, 16, 128, 128) == 0        # one pass
+    assert lib.gdla_decode_workspace_size(64, 16, 65536, 128) == 0      # window caps it
+    big = lib.gdla_decode_workspace_size(64, 16, 65536, 0)
+    assert big > 0 and big % 16 == 0
+    assert lib.gdla_decode_workspace_size(64, 16, 65536 * 2, 0) > big
+    assert lib.gdla_decode_workspace_size(0, 16, 100, 0) == 0
+    assert lib.gdla_decode_workspace_size(4, 16, -1, 0) == 0
+
+
+def test_decode_rejections(lib):
+    assert decode(lib, B=-1) == INVALID
+    assert decode(lib, group=2) == UNSUPPORTED
+    assert decode(lib, window=-2) == INVALID
+    assert decode(lib, max_len=0) == INVALID
+    assert decode(lib, cu=None) == INVALID
+    assert decode(lib, cu=A + 2) == MISALIGNED
+    for i in range(7):
+        ptrs = [A + k * (1 << 32) for k in range(7)]
+        ptrs[i] = None
+        assert decode(lib, ptrs) == INVALID
+        ptrs[i] = A + 4 + i * (1 << 32)
+        assert decode(lib, ptrs) == MISALIGNED
+    need = lib.gdla_decode_workspace_size(2, 16, 65536, 0)
+    assert decode(lib, max_len=65536) == WORKSPACE
+    assert decode(lib, max_len=65536, ws=A + 0x800000000, ws_bytes=need - 1) == WORKSPACE
+    assert decode(lib, max_len=65536, ws=A + 0x800000008, ws_bytes=need) == MISALIGNED
+
+
+def test_decode_empty_is_noop(lib):
+    assert decode(lib, [None] * 7, cu=None, B=0) == OK
