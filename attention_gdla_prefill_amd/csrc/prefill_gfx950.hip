@@ -9,9 +9,10 @@
 //      causal layer, t-W+1..t for a sliding-window layer (aitrends.kr,
 //      context-parallel paragraph: full attention costs Theta(L^2), sliding
 //      window Theta(LW)); tiles outside the band are never loaded;
-//   2. K and V tiles stream HBM -> registers -> LDS, double buffered, shared
-//      by the 4 waves and all 5 heads; V is stored transposed so that the P*V
-//      contraction reads 16 contiguous bytes per lane;
+//   2. K and V tiles stream HBM -> LDS with direct (register-free) 16-byte
+//      loads, one tile ahead into the other of two buffers, shared by the 4
+//      waves and all 5 heads; V stays row-major and the P*V operand is read
+//      with the gfx950 LDS transpose read (ds_read_b64_tr_b16);
 //   3. S^T = K Q^T on the matrix cores (bf16 in, fp32 out), causal / window
 //      mask on the tiles that straddle the band edge only;
 //   4. online softmax in base 2 with the scale folded in and row sums kept
@@ -38,9 +39,35 @@ namespace gdla {
 constexpr int PF_BM = 64;             // query tokens per workgroup
 constexpr int PF_BN = 64;             // keys per LDS tile
 constexpr int PF_THREADS = 256;       // 4 waves
-constexpr int KS_ROW = D_QK + 8;      // bf16 per K row in LDS (16-byte pad against bank conflicts)
-constexpr int VT_ROW = PF_BN + 8;     // bf16 per transposed V row in LDS
 constexpr int KK_STEPS = D_QK / 32;   // MFMA k-steps over the query-key dim
+// LDS rows carry one 16-byte pad chunk so that the fragment reads of 16
+// consecutive rows spread over all banks (K: 400-byte rows, V: 272-byte rows).
+constexpr int KS_CHUNKS = D_QK / 8 + 1;            // 25 chunks of 16 bytes per K row
+constexpr int VS_CHUNKS = D_V / 8 + 1;             // 17 chunks per V row
+constexpr int KS_ROW = KS_CHUNKS * 8;              // bf16 per K row in LDS
+constexpr int VS_ROW = VS_CHUNKS * 8;              // bf16 per V row in LDS
+constexpr int K_TILE_LOADS = PF_BN * KS_CHUNKS / 64;   // 25 wave-wide 1 KB loads per K tile
+constexpr int V_TILE_LOADS = PF_BN * VS_CHUNKS / 64;   // 17 per V tile
+static_assert(PF_BN * KS_CHUNKS % 64 == 0 && PF_BN * VS_CHUNKS % 64 == 0, "whole wave loads");
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
+
+// One 16-byte global -> LDS copy per lane; lane l writes lds_base + 16*l.
+__device__ __forceinline__ void copy16_to_lds(const void *g, __bf16 *lds_base) {
+    __builtin_amdgcn_global_load_lds(g, (lds_void_t *)lds_base, 16, 0, 0);
+}
+
+// Wait until this wave's outstanding vector-memory loads (including the
+// direct-to-LDS copies) have completed: s_waitcnt vmcnt(0).
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Transposing LDS read: within each 16-lane group, lane i receives element
+// i % 4 of the 8-byte words fetched by lanes 4e + i/4 (e = 0..3).
+__device__ __forceinline__ s16x4 lds_read_tr16(const __bf16 *p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t *)(p));
+}
 
 struct PrefillParams {
     const __bf16 *qs, *qn, *k, *v, *lam, *gate;
@@ -68,8 +95,13 @@ __device__ __forceinline__ void map_item(int bid, int n_hi, int n_qt, bool causa
 }
 
 __global__ __launch_bounds__(PF_THREADS, 1) void prefill_kernel(PrefillParams p) {
-    __shared__ __attribute__((aligned(16))) __bf16 Ks[2][PF_BN * KS_ROW];
-    __shared__ __attribute__((aligned(16))) __bf16 Vt[2][D_V * VT_ROW];
+    // two K and two V tile buffers as separate objects, so that reads of one
+    // buffer are never ordered behind the copies in flight into the other
+    __shared__ __attribute__((aligned(16))) __bf16 Ks0[PF_BN * KS_ROW];
+    __shared__ __attribute__((aligned(16))) __bf16 Ks1[PF_BN * KS_ROW];
+    __shared__ __attribute__((aligned(16))) __bf16 Vs0[PF_BN * VS_ROW];
+    __shared__ __attribute__((aligned(16))) __bf16 Vs1[PF_BN * VS_ROW];
+    __shared__ int restart_flag;
 
     const int T = p.T, n_kv = p.n_kv, window = p.window;
     const int n_sig = n_kv * GROUP;
@@ -83,6 +115,35 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_kernel(PrefillParams p)
     const int tw = t0 + 16 * wave;    // first query token of this wave
     const int tq = tw + r;            // query token of this lane
     const long seq0 = (long)b * T;    // first row of sequence b
+
+    // ---- key tiles this query tile can see
+    const int key_last = min(t0 + PF_BM, T) - 1;
+    const int key_first = window > 0 ? max(0, t0 - window + 1) : 0;
+    const int kt_lo = key_first / PF_BN, kt_hi = key_last / PF_BN;
+
+    // ---- direct HBM -> LDS copy of key tile kt; rows past the sequence end
+    // are read from its last row (those keys are always masked)
+    const __bf16 *kg = p.k + (seq0 * n_kv + j) * D_QK;
+    const __bf16 *vg = p.v + (seq0 * n_kv + j) * D_V;
+    const long krow = (long)n_kv * D_QK, vrow = (long)n_kv * D_V;
+    auto issue_tile = [&](int kt, __bf16 *ks, __bf16 *vs) {
+        const int kbase = kt * PF_BN;
+        for (int i = wave; i < K_TILE_LOADS; i += 4) {
+            const int u = i * 64 + lane;
+            const int row = u / KS_CHUNKS, ch = u % KS_CHUNKS;
+            const int key = min(kbase + row, T - 1);
+            const int src_ch = ch < KS_CHUNKS - 1 ? ch : ch - 1;      // pad chunk: any data
+            copy16_to_lds(kg + key * krow + 8 * src_ch, ks + i * 512);
+        }
+        for (int i = wave; i < V_TILE_LOADS; i += 4) {
+            const int u = i * 64 + lane;
+            const int row = u / VS_CHUNKS, ch = u % VS_CHUNKS;
+            const int key = min(kbase + row, T - 1);
+            const int src_ch = ch < VS_CHUNKS - 1 ? ch : ch - 1;
+            copy16_to_lds(vg + key * vrow + 8 * src_ch, vs + i * 512);
+        }
+    };
+    issue_tile(kt_lo, Ks0, Vs0);
 
     // ---- queries: B operand fragments, lane holds Q[tq][32kk + 8g .. +7]
     bf16x8 qf[HEADS][KK_STEPS];
@@ -102,45 +163,6 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_kernel(PrefillParams p)
         }
     }
 
-    // ---- key tiles this query tile can see
-    const int key_last = min(t0 + PF_BM, T) - 1;
-    const int key_first = window > 0 ? max(0, t0 - window + 1) : 0;
-    const int kt_lo = key_first / PF_BN, kt_hi = key_last / PF_BN;
-
-    // ---- tile staging: K as 6 16-byte chunks per thread, V as a 4-key x 8-column block
-    u32x4 kreg[6], vreg[4];
-    const int v_kg = tid >> 4, v_cc = tid & 15;
-    auto load_tile = [&](int kt) {
-        const int kbase = kt * PF_BN;
-#pragma unroll
-        for (int i = 0; i < 6; ++i) {
-            const int c = tid + PF_THREADS * i;
-            const int key = kbase + c / 24, dc = c % 24;
-            kreg[i] = key < T ? ldg16(p.k + ((seq0 + key) * n_kv + j) * D_QK + 8 * dc)
-                              : u32x4{0, 0, 0, 0};
-        }
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-            const int key = kbase + 4 * v_kg + rr;
-            vreg[rr] = key < T ? ldg16(p.v + ((seq0 + key) * n_kv + j) * D_V + 8 * v_cc)
-                               : u32x4{0, 0, 0, 0};
-        }
-    };
-    auto store_tile = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < 6; ++i) {
-            const int c = tid + PF_THREADS * i;
-            *reinterpret_cast<u32x4 *>(&Ks[buf][(c / 24) * KS_ROW + 8 * (c % 24)]) = kreg[i];
-        }
-        u32x2 cols[8];
-        transpose4x8(vreg, cols);
-        const int kl0 = 4 * v_kg;
-        const int pos = 32 * (kl0 >> 5) + vt_pos(kl0 & 31);
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-            *reinterpret_cast<u32x2 *>(&Vt[buf][(8 * v_cc + e) * VT_ROW + pos]) = cols[e];
-    };
-
     // ---- softmax state (per lane: query tq of each head)
     float m_ref[HEADS], l_part[HEADS];
     f32x4 o[HEADS][D_V / 16];
@@ -152,19 +174,14 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_kernel(PrefillParams p)
         for (int cb = 0; cb < D_V / 16; ++cb) o[h][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
     const float c_log2 = p.scale_log2;
-    __shared__ int restart_flag;
     if (tid == 0) restart_flag = 0;
     bool wave_restart = false;        // this wave met a key beyond its reference + RESTART_LOG2
 
-    load_tile(kt_lo);
-    store_tile(0);
-    __syncthreads();
-
-    for (int kt = kt_lo; kt <= kt_hi; ++kt) {
-        const int buf = (kt - kt_lo) & 1;
-        const bool more = kt < kt_hi;
-
-#pragma unroll
+    // ---- one key tile: 2 slices of 32 keys, each S^T = K Q^T, softmax, O^T += V^T P^T
+    auto compute_tile = [&](int kt, const __bf16 *ks, const __bf16 *vs) {
+        // kept rolled: unrolling lets the scheduler overlap two slices, which
+        // doubles the live scores and spills
+#pragma unroll 1
         for (int sub = 0; sub < 2; ++sub) {
             const int kb0 = kt * PF_BN + 32 * sub;     // first key of this 32-key slice
             // wave-uniform skips: no valid query, all keys in the future, all keys too old
@@ -172,40 +189,52 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_kernel(PrefillParams p)
             if (window > 0 && kb0 + 31 < tw - window + 1) continue;
             const bool need_mask = (kb0 + 31 > tw) || (window > 0 && kb0 < tw + 16 - window);
 
-            // S^T = K Q^T over 2 blocks of 16 keys
+            // S^T = K Q^T over 2 blocks of 16 keys; K fragments one k-step ahead
+            const __bf16 *krd = ks + (32 * sub + r) * KS_ROW + 8 * g;
             f32x4 s[HEADS][2];
-#pragma unroll
-            for (int h = 0; h < HEADS; ++h) s[h][0] = s[h][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+            const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+            bf16x8 ka0 = *reinterpret_cast<const bf16x8 *>(krd);
+            bf16x8 ka1 = *reinterpret_cast<const bf16x8 *>(krd + 16 * KS_ROW);
 #pragma unroll
             for (int kk = 0; kk < KK_STEPS; ++kk) {
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
-                    const bf16x8 a = *reinterpret_cast<const bf16x8 *>(
-                        &Ks[buf][(32 * sub + 16 * kb + r) * KS_ROW + 32 * kk + 8 * g]);
-#pragma unroll
-                    for (int h = 0; h < HEADS; ++h) s[h][kb] = mfma16(a, qf[h][kk], s[h][kb]);
+                bf16x8 na0 = ka0, na1 = ka1;
+                if (kk + 1 < KK_STEPS) {
+                    na0 = *reinterpret_cast<const bf16x8 *>(krd + 32 * (kk + 1));
+                    na1 = *reinterpret_cast<const bf16x8 *>(krd + 16 * KS_ROW + 32 * (kk + 1));
                 }
+#pragma unroll
+                for (int h = 0; h < HEADS; ++h) s[h][0] = mfma16(ka0, qf[h][kk], kk == 0 ? zero4 : s[h][0]);
+#pragma unroll
+                for (int h = 0; h < HEADS; ++h) s[h][1] = mfma16(ka1, qf[h][kk], kk == 0 ? zero4 : s[h][1]);
+                ka0 = na0;
+                ka1 = na1;
             }
+            // scores of this lane (query tq, keys kb0 + 16kb + 4g + e) as plain floats;
+            // masked keys become -inf on the copies, the accumulators stay untouched
+            float sv[HEADS][8];
+#pragma unroll
+            for (int h = 0; h < HEADS; ++h)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    sv[h][e] = s[h][0][e];
+                    sv[h][4 + e] = s[h][1][e];
+                }
             if (need_mask) {
 #pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
+                for (int i = 0; i < 8; ++i) {
+                    const int key = kb0 + 16 * (i >> 2) + 4 * g + (i & 3);
+                    const bool vis = key <= tq && (window == 0 || key > tq - window);
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int key = kb0 + 16 * kb + 4 * g + e;
-                        const bool vis = key <= tq && (window == 0 || key > tq - window);
-                        if (!vis) {
-#pragma unroll
-                            for (int h = 0; h < HEADS; ++h) s[h][kb][e] = -INFINITY;
-                        }
-                    }
+                    for (int h = 0; h < HEADS; ++h) sv[h][i] = vis ? sv[h][i] : -INFINITY;
+                }
             }
 
             // reference maxima: set on first sight, restart on a jump beyond RESTART_LOG2
             bool jump = false;
 #pragma unroll
             for (int h = 0; h < HEADS; ++h) {
-                float mx = fmaxf(fmaxf(fmaxf(s[h][0][0], s[h][0][1]), fmaxf(s[h][0][2], s[h][0][3])),
-                                 fmaxf(fmaxf(s[h][1][0], s[h][1][1]), fmaxf(s[h][1][2], s[h][1][3])));
+                float mx = fmaxf(fmaxf(fmaxf(sv[h][0], sv[h][1]), fmaxf(sv[h][2], sv[h][3])),
+                                 fmaxf(fmaxf(sv[h][4], sv[h][5]), fmaxf(sv[h][6], sv[h][7])));
                 mx = group4_max(mx) * c_log2;
                 if (m_ref[h] == -INFINITY) {
                     m_ref[h] = mx;
@@ -225,33 +254,61 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_kernel(PrefillParams p)
                 const float mref = m_ref[h] == -INFINITY ? 0.f : m_ref[h];
                 float pv[8];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    pv[e] = fast_exp2(fmaf(s[h][0][e], c_log2, -mref));
-                    pv[4 + e] = fast_exp2(fmaf(s[h][1][e], c_log2, -mref));
-                }
+                for (int i = 0; i < 8; ++i) pv[i] = fast_exp2(fmaf(sv[h][i], c_log2, -mref));
                 l_part[h] += ((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7]));
                 u32x4 w = {pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]),
                            pack_bf16x2(pv[4], pv[5]), pack_bf16x2(pv[6], pv[7])};
                 pb[h] = __builtin_bit_cast(bf16x8, w);
             }
 
-            // O^T += V^T P^T
+            // O^T += V^T P^T.  The A operand (16 columns c x 32 keys) comes from
+            // two transposing reads of row-major V: lane (r, g) receives
+            // V[4g + e][16cb + r] and V[16 + 4g + e][16cb + r], e = 0..3 -- the
+            // keys its P^T fragment holds in k-slots 8g..8g+7.
+            const __bf16 *vrd = vs + (32 * sub + 4 * g + (r >> 2)) * VS_ROW + 4 * (r & 3);
+            auto vfrag = [&](int cb) {
+                const s16x4 lo = lds_read_tr16(vrd + 16 * cb);
+                const s16x4 hi4 = lds_read_tr16(vrd + 16 * VS_ROW + 16 * cb);
+                const s16x4 v8[2] = {lo, hi4};
+                return __builtin_bit_cast(bf16x8, v8);
+            };
+            bf16x8 va = vfrag(0);
 #pragma unroll
             for (int cb = 0; cb < D_V / 16; ++cb) {
-                const bf16x8 a = *reinterpret_cast<const bf16x8 *>(
-                    &Vt[buf][(16 * cb + r) * VT_ROW + 32 * sub + 8 * g]);
+                bf16x8 nv = va;
+                if (cb + 1 < D_V / 16) nv = vfrag(cb + 1);
 #pragma unroll
-                for (int h = 0; h < HEADS; ++h) o[h][cb] = mfma16(a, pb[h], o[h][cb]);
+                for (int h = 0; h < HEADS; ++h) o[h][cb] = mfma16(va, pb[h], o[h][cb]);
+                va = nv;
             }
         }
+    };
 
-        if (more) {
-            load_tile(kt + 1);
-            store_tile(buf ^ 1);
+    // ---- the key-tile loop, unrolled by two so that each buffer is named
+    // statically; tile kt+1 is copied in while tile kt is computed
+    wait_vmem();
+    __syncthreads();
+    int kt = kt_lo;
+    while (kt <= kt_hi) {
+        bool restart = false;
+#pragma unroll
+        for (int half = 0; half < 2 && kt <= kt_hi; ++half, ++kt) {
+            const __bf16 *ks = half == 0 ? Ks0 : Ks1;
+            const __bf16 *vs = half == 0 ? Vs0 : Vs1;
+            if (kt < kt_hi) {
+                if (half == 0) issue_tile(kt + 1, Ks1, Vs1);
+                else issue_tile(kt + 1, Ks0, Vs0);
+            }
+            compute_tile(kt, ks, vs);
+            if (wave_restart && lane == 0) restart_flag = 1;
+            wait_vmem();
+            __syncthreads();
+            if (__builtin_amdgcn_readfirstlane(restart_flag)) {
+                restart = true;
+                break;
+            }
         }
-        if (wave_restart && lane == 0) restart_flag = 1;
-        __syncthreads();
-        if (__builtin_amdgcn_readfirstlane(restart_flag)) {
+        if (restart) {
             // some row met a key far above its reference: redo the pass from the
             // first tile with the raised references (accumulators start from zero)
             __syncthreads();                       // every wave has read the flag
@@ -263,10 +320,10 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_kernel(PrefillParams p)
                 for (int cb = 0; cb < D_V / 16; ++cb) o[h][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
             }
             wave_restart = false;
-            load_tile(kt_lo);
-            store_tile(0);
+            kt = kt_lo;
+            issue_tile(kt_lo, Ks0, Vs0);
+            wait_vmem();
             __syncthreads();
-            kt = kt_lo - 1;
         }
     }
 
