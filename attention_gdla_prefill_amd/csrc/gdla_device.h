@@ -31,12 +31,16 @@ constexpr float LOG2E = 1.4426950408889634f;
 // softmax reference is only raised when a new score exceeds it by more than
 // this, so unnormalised weights stay below 2^8 and fp32 cannot overflow.
 constexpr float RESCALE_LOG2 = 8.0f;
-// Prefill keeps each row's reference fixed: weights exp2(x - ref) may reach
-// 2^64 (row sums stay below 2^81 for 2^17 keys, far from fp32's 2^128).  A
-// larger jump restarts the pass with the reference raised to the new maximum
-// plus a headroom, so that slowly growing scores do not restart repeatedly;
-// the largest weight is then >= 2^-32, still far from underflow.
-constexpr float RESTART_LOG2 = 64.0f;
+// Prefill keeps each row's reference fixed.  A slice whose weights
+// exp2(x - ref) of one lane sum above 2^64 (so some weight exceeds 2^61)
+// restarts the pass; the restart raises every row whose maximum exceeds its
+// reference by more than 2^60 -- which includes the row that tripped the
+// check -- to that maximum plus a headroom, so slowly growing scores do not
+// restart repeatedly.  Weights thus stay below 2^64 (row sums below 2^81 for
+// 2^17 keys, far from fp32's 2^128) and the largest weight of a row stays
+// above 2^-32.
+constexpr float RESTART_SUM = 0x1p64f;
+constexpr float RAISE_LOG2 = 60.0f;
 constexpr float RESTART_HEADROOM_LOG2 = 32.0f;
 
 __device__ __forceinline__ f32x4 mfma16(const bf16x8 &a, const bf16x8 &b, const f32x4 &c) {
@@ -60,9 +64,13 @@ __device__ __forceinline__ float group4_sum(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Two floats -> packed bf16 pair, round to nearest even (one v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    __bf16 a = (__bf16)lo, b = (__bf16)hi;   // round to nearest even
-    return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+    const f32x2 v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }

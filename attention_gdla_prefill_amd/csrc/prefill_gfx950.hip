@@ -17,11 +17,11 @@
 //      mask on the tiles that straddle the band edge only;
 //   4. online softmax in base 2 with the scale folded in and row sums kept
 //      per lane.  Each row's reference maximum is fixed by the first visible
-//      keys it meets; later keys may exceed it by up to 2^64 before the
-//      workgroup restarts its pass with a raised reference (rare: it needs a
-//      logit jump of ~44 in natural units).  The accumulators are thus never
-//      rescaled inside the loop, which keeps them in the matrix-core register
-//      file;
+//      keys it meets (the row maximum is not computed after that); later
+//      weights may grow to ~2^61 before the workgroup restarts its pass with
+//      a raised reference (rare: it needs a logit jump of ~42 in natural
+//      units).  The accumulators are thus never rescaled inside the loop,
+//      which keeps them in the matrix-core register file;
 //   5. O^T += V^T P^T on the matrix cores;
 //   6. epilogue in registers: H = O / l, D = H_S - lambda * H_N (each noise
 //      row repeated to its 4 signal heads), out = gate * D, rounded to bf16
@@ -175,7 +175,7 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_kernel(PrefillParams p)
     }
     const float c_log2 = p.scale_log2;
     if (tid == 0) restart_flag = 0;
-    bool wave_restart = false;        // this wave met a key beyond its reference + RESTART_LOG2
+    bool wave_restart = false;        // this wave met a weight beyond the reference range
 
     // ---- one key tile: 2 slices of 32 keys, each S^T = K Q^T, softmax, O^T += V^T P^T
     auto compute_tile = [&](int kt, const __bf16 *ks, const __bf16 *vs) {
@@ -209,56 +209,60 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_kernel(PrefillParams p)
                 ka0 = na0;
                 ka1 = na1;
             }
-            // scores of this lane (query tq, keys kb0 + 16kb + 4g + e) as plain floats;
-            // masked keys become -inf on the copies, the accumulators stay untouched
-            float sv[HEADS][8];
-#pragma unroll
-            for (int h = 0; h < HEADS; ++h)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    sv[h][e] = s[h][0][e];
-                    sv[h][4 + e] = s[h][1][e];
-                }
+            // visibility of this lane's 8 keys kb0 + 16*(i/4) + 4g + i%4 (edge slices only)
+            unsigned vis = 0xffu;
             if (need_mask) {
+                vis = 0;
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
                     const int key = kb0 + 16 * (i >> 2) + 4 * g + (i & 3);
-                    const bool vis = key <= tq && (window == 0 || key > tq - window);
-#pragma unroll
-                    for (int h = 0; h < HEADS; ++h) sv[h][i] = vis ? sv[h][i] : -INFINITY;
+                    if (key <= tq && (window == 0 || key > tq - window)) vis |= 1u << i;
                 }
             }
+            // largest visible score of this lane's row, in log2 units
+            auto row_max = [&](int h) {
+                float mx = -INFINITY;
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    mx = fmaxf(mx, (vis >> i) & 1 ? s[h][i >> 2][i & 3] : -INFINITY);
+                return group4_max(mx) * c_log2;
+            };
 
-            // reference maxima: set on first sight, restart on a jump beyond RESTART_LOG2
+            // base-2 softmax against the row's fixed reference; the reference is
+            // the first visible maximum, so the max is only taken until it is set
             bool jump = false;
-#pragma unroll
-            for (int h = 0; h < HEADS; ++h) {
-                float mx = fmaxf(fmaxf(fmaxf(sv[h][0], sv[h][1]), fmaxf(sv[h][2], sv[h][3])),
-                                 fmaxf(fmaxf(sv[h][4], sv[h][5]), fmaxf(sv[h][6], sv[h][7])));
-                mx = group4_max(mx) * c_log2;
-                if (m_ref[h] == -INFINITY) {
-                    m_ref[h] = mx;
-                } else if (mx > m_ref[h] + RESTART_LOG2) {
-                    m_ref[h] = mx + RESTART_HEADROOM_LOG2;
-                    jump = true;
-                }
-            }
-            if (__any(jump)) {
-                wave_restart = true;
-                continue;
-            }
-
             bf16x8 pb[HEADS];
 #pragma unroll
             for (int h = 0; h < HEADS; ++h) {
+                if (__any(m_ref[h] == -INFINITY)) {
+                    const float mx = row_max(h);
+                    if (m_ref[h] == -INFINITY) m_ref[h] = mx;
+                }
                 const float mref = m_ref[h] == -INFINITY ? 0.f : m_ref[h];
                 float pv[8];
 #pragma unroll
-                for (int i = 0; i < 8; ++i) pv[i] = fast_exp2(fmaf(sv[h][i], c_log2, -mref));
-                l_part[h] += ((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7]));
+                for (int i = 0; i < 8; ++i) pv[i] = fast_exp2(fmaf(s[h][i >> 2][i & 3], c_log2, -mref));
+                if (need_mask) {
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) pv[i] = (vis >> i) & 1 ? pv[i] : 0.f;
+                }
+                const float ps = ((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7]));
+                jump |= ps > RESTART_SUM;
+                l_part[h] += ps;
                 u32x4 w = {pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]),
                            pack_bf16x2(pv[4], pv[5]), pack_bf16x2(pv[6], pv[7])};
                 pb[h] = __builtin_bit_cast(bf16x8, w);
+            }
+            if (__any(jump)) {
+                // a weight beyond 2^61: raise the reference of every row whose
+                // maximum is more than 2^60 above it, and redo the pass
+#pragma unroll
+                for (int h = 0; h < HEADS; ++h) {
+                    const float mx = row_max(h);
+                    if (mx > m_ref[h] + RAISE_LOG2) m_ref[h] = mx + RESTART_HEADROOM_LOG2;
+                }
+                wave_restart = true;
+                continue;
             }
 
             // O^T += V^T P^T.  The A operand (16 columns c x 32 keys) comes from
