@@ -189,26 +189,45 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_kernel(PrefillParams p)
             if (window > 0 && kb0 + 31 < tw - window + 1) continue;
             const bool need_mask = (kb0 + 31 > tw) || (window > 0 && kb0 < tw + 16 - window);
 
-            // S^T = K Q^T over 2 blocks of 16 keys; K fragments one k-step ahead
+            // S^T = K Q^T, first the 16 keys of block 0 for all heads, then block 1,
+            // so that block 0's weights can be formed while block 1 is multiplied.
+            // K fragments are read one k-step ahead.
             const __bf16 *krd = ks + (32 * sub + r) * KS_ROW + 8 * g;
             f32x4 s[HEADS][2];
             const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
-            bf16x8 ka0 = *reinterpret_cast<const bf16x8 *>(krd);
-            bf16x8 ka1 = *reinterpret_cast<const bf16x8 *>(krd + 16 * KS_ROW);
+            auto qk_block = [&](int kb) {
+                const __bf16 *kr = krd + 16 * kb * KS_ROW;
+                bf16x8 ka = *reinterpret_cast<const bf16x8 *>(kr);
 #pragma unroll
-            for (int kk = 0; kk < KK_STEPS; ++kk) {
-                bf16x8 na0 = ka0, na1 = ka1;
-                if (kk + 1 < KK_STEPS) {
-                    na0 = *reinterpret_cast<const bf16x8 *>(krd + 32 * (kk + 1));
-                    na1 = *reinterpret_cast<const bf16x8 *>(krd + 16 * KS_ROW + 32 * (kk + 1));
+                for (int kk = 0; kk < KK_STEPS; ++kk) {
+                    bf16x8 na = ka;
+                    if (kk + 1 < KK_STEPS) na = *reinterpret_cast<const bf16x8 *>(kr + 32 * (kk + 1));
+#pragma unroll
+                    for (int h = 0; h < HEADS; ++h)
+                        s[h][kb] = mfma16(ka, qf[h][kk], kk == 0 ? zero4 : s[h][kb]);
+                    ka = na;
                 }
+            };
+            // weights of key block kb against the fixed references: p = 2^(x*c - ref)
+            float ps[HEADS];
+            uint32_t pw[HEADS][4];
+            auto weights = [&](int kb, unsigned vis) {
 #pragma unroll
-                for (int h = 0; h < HEADS; ++h) s[h][0] = mfma16(ka0, qf[h][kk], kk == 0 ? zero4 : s[h][0]);
+                for (int h = 0; h < HEADS; ++h) {
+                    const float mref = m_ref[h] == -INFINITY ? 0.f : m_ref[h];
+                    float pv[4];
 #pragma unroll
-                for (int h = 0; h < HEADS; ++h) s[h][1] = mfma16(ka1, qf[h][kk], kk == 0 ? zero4 : s[h][1]);
-                ka0 = na0;
-                ka1 = na1;
-            }
+                    for (int e = 0; e < 4; ++e) {
+                        pv[e] = fast_exp2(fmaf(s[h][kb][e], c_log2, -mref));
+                        pv[e] = (vis >> (4 * kb + e)) & 1 ? pv[e] : 0.f;
+                    }
+                    const float part = (pv[0] + pv[1]) + (pv[2] + pv[3]);
+                    ps[h] = kb == 0 ? part : ps[h] + part;
+                    pw[h][2 * kb] = pack_bf16x2(pv[0], pv[1]);
+                    pw[h][2 * kb + 1] = pack_bf16x2(pv[2], pv[3]);
+                }
+            };
+
             // visibility of this lane's 8 keys kb0 + 16*(i/4) + 4g + i%4 (edge slices only)
             unsigned vis = 0xffu;
             if (need_mask) {
@@ -228,34 +247,37 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_kernel(PrefillParams p)
                 return group4_max(mx) * c_log2;
             };
 
-            // base-2 softmax against the row's fixed reference; the reference is
-            // the first visible maximum, so the max is only taken until it is set
-            bool jump = false;
-            bf16x8 pb[HEADS];
+            bool unset = false;
 #pragma unroll
-            for (int h = 0; h < HEADS; ++h) {
-                if (__any(m_ref[h] == -INFINITY)) {
-                    const float mx = row_max(h);
-                    if (m_ref[h] == -INFINITY) m_ref[h] = mx;
+            for (int h = 0; h < HEADS; ++h) unset |= m_ref[h] == -INFINITY;
+            if (!need_mask && !__any(unset)) {
+                // common case: every key visible, every reference set; one basic
+                // block, so block 0's exponentials overlap block 1's MFMAs
+                qk_block(0);
+                weights(0, 0xffu);
+                qk_block(1);
+                weights(1, 0xffu);
+            } else {
+                // band edge or rows without a reference yet
+                qk_block(0);
+                qk_block(1);
+#pragma unroll
+                for (int h = 0; h < HEADS; ++h) {
+                    if (__any(m_ref[h] == -INFINITY)) {
+                        const float mx = row_max(h);
+                        if (m_ref[h] == -INFINITY) m_ref[h] = mx;
+                    }
                 }
-                const float mref = m_ref[h] == -INFINITY ? 0.f : m_ref[h];
-                float pv[8];
-#pragma unroll
-                for (int i = 0; i < 8; ++i) pv[i] = fast_exp2(fmaf(s[h][i >> 2][i & 3], c_log2, -mref));
-                if (need_mask) {
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) pv[i] = (vis >> i) & 1 ? pv[i] : 0.f;
-                }
-                const float ps = ((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7]));
-                jump |= ps > RESTART_SUM;
-                l_part[h] += ps;
-                u32x4 w = {pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]),
-                           pack_bf16x2(pv[4], pv[5]), pack_bf16x2(pv[6], pv[7])};
-                pb[h] = __builtin_bit_cast(bf16x8, w);
+                weights(0, vis);
+                weights(1, vis);
             }
+
+            bool jump = false;
+#pragma unroll
+            for (int h = 0; h < HEADS; ++h) jump |= ps[h] > RESTART_SUM;
             if (__any(jump)) {
                 // a weight beyond 2^61: raise the reference of every row whose
-                // maximum is more than 2^60 above it, and redo the pass
+                // visible maximum is more than 2^60 above it, and redo the pass
 #pragma unroll
                 for (int h = 0; h < HEADS; ++h) {
                     const float mx = row_max(h);
@@ -263,6 +285,13 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_kernel(PrefillParams p)
                 }
                 wave_restart = true;
                 continue;
+            }
+            bf16x8 pb[HEADS];
+#pragma unroll
+            for (int h = 0; h < HEADS; ++h) {
+                l_part[h] += ps[h];
+                const u32x4 w = {pw[h][0], pw[h][1], pw[h][2], pw[h][3]};
+                pb[h] = __builtin_bit_cast(bf16x8, w);
             }
 
             // O^T += V^T P^T.  The A operand (16 columns c x 32 keys) comes from
