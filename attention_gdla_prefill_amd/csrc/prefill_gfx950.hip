@@ -40,14 +40,17 @@ constexpr int PF_BM = 64;             // query tokens per workgroup
 constexpr int PF_BN = 64;             // keys per LDS tile
 constexpr int PF_THREADS = 256;       // 4 waves
 constexpr int KK_STEPS = D_QK / 32;   // MFMA k-steps over the query-key dim
-// LDS rows carry one 16-byte pad chunk so that the fragment reads of 16
-// consecutive rows spread over all banks (K: 400-byte rows, V: 272-byte rows).
-constexpr int KS_CHUNKS = D_QK / 8 + 1;            // 25 chunks of 16 bytes per K row
-constexpr int VS_CHUNKS = D_V / 8 + 1;             // 17 chunks per V row
+// LDS rows carry a 32-byte pad so that the fragment reads of 16 consecutive
+// rows spread over all banks (K: 416-byte rows, V: 288-byte rows).  Measured
+// on gfx950: a 16-byte pad still leaves half the LDS cycles in bank conflicts
+// for both the 16-byte K reads and the transposing V reads; 32 bytes removes them.
+constexpr int ROW_PAD_CHUNKS = 2;
+constexpr int KS_CHUNKS = D_QK / 8 + ROW_PAD_CHUNKS;   // 26 chunks of 16 bytes per K row
+constexpr int VS_CHUNKS = D_V / 8 + ROW_PAD_CHUNKS;    // 18 chunks per V row
 constexpr int KS_ROW = KS_CHUNKS * 8;              // bf16 per K row in LDS
 constexpr int VS_ROW = VS_CHUNKS * 8;              // bf16 per V row in LDS
-constexpr int K_TILE_LOADS = PF_BN * KS_CHUNKS / 64;   // 25 wave-wide 1 KB loads per K tile
-constexpr int V_TILE_LOADS = PF_BN * VS_CHUNKS / 64;   // 17 per V tile
+constexpr int K_TILE_LOADS = PF_BN * KS_CHUNKS / 64;   // 26 wave-wide 1 KB loads per K tile
+constexpr int V_TILE_LOADS = PF_BN * VS_CHUNKS / 64;   // 18 per V tile
 static_assert(PF_BN * KS_CHUNKS % 64 == 0 && PF_BN * VS_CHUNKS % 64 == 0, "whole wave loads");
 
 typedef __attribute__((address_space(3))) void lds_void_t;
@@ -132,14 +135,14 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_kernel(PrefillParams p)
             const int u = i * 64 + lane;
             const int row = u / KS_CHUNKS, ch = u % KS_CHUNKS;
             const int key = min(kbase + row, T - 1);
-            const int src_ch = ch < KS_CHUNKS - 1 ? ch : ch - 1;      // pad chunk: any data
+            const int src_ch = min(ch, D_QK / 8 - 1);                 // pad chunks: any data
             copy16_to_lds(kg + key * krow + 8 * src_ch, ks + i * 512);
         }
         for (int i = wave; i < V_TILE_LOADS; i += 4) {
             const int u = i * 64 + lane;
             const int row = u / VS_CHUNKS, ch = u % VS_CHUNKS;
             const int key = min(kbase + row, T - 1);
-            const int src_ch = ch < VS_CHUNKS - 1 ? ch : ch - 1;
+            const int src_ch = min(ch, D_V / 8 - 1);
             copy16_to_lds(vg + key * vrow + 8 * src_ch, vs + i * 512);
         }
     };
