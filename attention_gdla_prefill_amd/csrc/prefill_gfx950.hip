@@ -49,9 +49,14 @@ constexpr int KS_CHUNKS = D_QK / 8 + ROW_PAD_CHUNKS;   // 26 chunks of 16 bytes 
 constexpr int VS_CHUNKS = D_V / 8 + ROW_PAD_CHUNKS;    // 18 chunks per V row
 constexpr int KS_ROW = KS_CHUNKS * 8;              // bf16 per K row in LDS
 constexpr int VS_ROW = VS_CHUNKS * 8;              // bf16 per V row in LDS
-constexpr int K_TILE_LOADS = PF_BN * KS_CHUNKS / 64;   // 26 wave-wide 1 KB loads per K tile
-constexpr int V_TILE_LOADS = PF_BN * VS_CHUNKS / 64;   // 18 per V tile
-static_assert(PF_BN * KS_CHUNKS % 64 == 0 && PF_BN * VS_CHUNKS % 64 == 0, "whole wave loads");
+// A tile is copied by wave-wide instructions that each cover whole rows: two
+// K rows (52 of 64 lanes) or three V rows (54 lanes), so a lane's row and
+// chunk within the instruction never change and pad chunks are skipped.
+constexpr int K_ROWS_PER_COPY = 2;
+constexpr int V_ROWS_PER_COPY = 3;
+constexpr int K_TILE_COPIES = PF_BN / K_ROWS_PER_COPY;                          // 32
+constexpr int V_TILE_COPIES = (PF_BN + V_ROWS_PER_COPY - 1) / V_ROWS_PER_COPY;  // 22
+static_assert(K_ROWS_PER_COPY * KS_CHUNKS <= 64 && V_ROWS_PER_COPY * VS_CHUNKS <= 64, "rows per copy");
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -129,21 +134,25 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_kernel(PrefillParams p)
     const __bf16 *kg = p.k + (seq0 * n_kv + j) * D_QK;
     const __bf16 *vg = p.v + (seq0 * n_kv + j) * D_V;
     const long krow = (long)n_kv * D_QK, vrow = (long)n_kv * D_V;
+    const int uwave = __builtin_amdgcn_readfirstlane(wave);
+    const int k_lr = lane / KS_CHUNKS, k_ch = lane % KS_CHUNKS;    // row within the copy, chunk
+    const int v_lr = lane / VS_CHUNKS, v_ch = lane % VS_CHUNKS;
+    const bool k_on = k_lr < K_ROWS_PER_COPY && k_ch < D_QK / 8;  // pad chunks are not copied
+    const bool v_on = v_lr < V_ROWS_PER_COPY && v_ch < D_V / 8;
     auto issue_tile = [&](int kt, __bf16 *ks, __bf16 *vs) {
         const int kbase = kt * PF_BN;
-        for (int i = wave; i < K_TILE_LOADS; i += 4) {
-            const int u = i * 64 + lane;
-            const int row = u / KS_CHUNKS, ch = u % KS_CHUNKS;
-            const int key = min(kbase + row, T - 1);
-            const int src_ch = min(ch, D_QK / 8 - 1);                 // pad chunks: any data
-            copy16_to_lds(kg + key * krow + 8 * src_ch, ks + i * 512);
+#pragma unroll
+        for (int c = 0; c < K_TILE_COPIES / 4; ++c) {
+            const int row0 = K_ROWS_PER_COPY * (uwave + 4 * c);
+            const int key = min(kbase + row0 + k_lr, T - 1);
+            if (k_on) copy16_to_lds(kg + key * krow + 8 * k_ch, ks + row0 * KS_ROW);
         }
-        for (int i = wave; i < V_TILE_LOADS; i += 4) {
-            const int u = i * 64 + lane;
-            const int row = u / VS_CHUNKS, ch = u % VS_CHUNKS;
-            const int key = min(kbase + row, T - 1);
-            const int src_ch = min(ch, D_V / 8 - 1);
-            copy16_to_lds(vg + key * vrow + 8 * src_ch, vs + i * 512);
+#pragma unroll
+        for (int c = 0; c < (V_TILE_COPIES + 3) / 4; ++c) {
+            const int row0 = V_ROWS_PER_COPY * (uwave + 4 * c);
+            const int key = min(kbase + row0 + v_lr, T - 1);
+            if (row0 < PF_BN && v_on && row0 + v_lr < PF_BN)
+                copy16_to_lds(vg + key * vrow + 8 * v_ch, vs + row0 * VS_ROW);
         }
     };
     issue_tile(kt_lo, Ks0, Vs0);
