@@ -10,8 +10,8 @@
 //      context-parallel paragraph: full attention costs Theta(L^2), sliding
 //      window Theta(LW)); tiles outside the band are never loaded;
 //   2. K and V tiles stream HBM -> LDS with direct (register-free) 16-byte
-//      loads, one tile ahead into the other of two buffers, shared by the 4
-//      waves and all 5 heads; V stays row-major and the P*V operand is read
+//      loads into a ring of three tile slots, two tiles ahead, shared by the
+//      4 waves and all 5 heads; V stays row-major and the P*V operand is read
 //      with the gfx950 LDS transpose read (ds_read_b64_tr_b16);
 //   3. S^T = K Q^T on the matrix cores (bf16 in, fp32 out), causal / window
 //      mask on the tiles that straddle the band edge only;
@@ -103,12 +103,10 @@ __device__ __forceinline__ void map_item(int bid, int n_hi, int n_qt, bool causa
 }
 
 __global__ __launch_bounds__(PF_THREADS, 1) void prefill_kernel(PrefillParams p) {
-    // two K and two V tile buffers as separate objects, so that reads of one
-    // buffer are never ordered behind the copies in flight into the other
-    __shared__ __attribute__((aligned(16))) __bf16 Ks0[PF_BN * KS_ROW];
-    __shared__ __attribute__((aligned(16))) __bf16 Ks1[PF_BN * KS_ROW];
-    __shared__ __attribute__((aligned(16))) __bf16 Vs0[PF_BN * VS_ROW];
-    __shared__ __attribute__((aligned(16))) __bf16 Vs1[PF_BN * VS_ROW];
+    // ring of three K and three V tile slots: tile kt is computed from slot
+    // kt % 3 while the copies of tile kt+1 land and those of kt+2 are issued
+    __shared__ __attribute__((aligned(16))) __bf16 Kring[3][PF_BN * KS_ROW];
+    __shared__ __attribute__((aligned(16))) __bf16 Vring[3][PF_BN * VS_ROW];
     __shared__ int restart_flag;
 
     const int T = p.T, n_kv = p.n_kv, window = p.window;
@@ -155,7 +153,8 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_kernel(PrefillParams p)
                 copy16_to_lds(vg + key * vrow + 8 * v_ch, vs + row0 * VS_ROW);
         }
     };
-    issue_tile(kt_lo, Ks0, Vs0);
+    issue_tile(kt_lo, Kring[0], Vring[0]);
+    if (kt_lo + 1 <= kt_hi) issue_tile(kt_lo + 1, Kring[1], Vring[1]);
 
     // ---- queries: B operand fragments, lane holds Q[tq][32kk + 8g .. +7]
     bf16x8 qf[HEADS][KK_STEPS];
@@ -329,33 +328,28 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_kernel(PrefillParams p)
         }
     };
 
-    // ---- the key-tile loop, unrolled by two so that each buffer is named
-    // statically; tile kt+1 is copied in while tile kt is computed
+    // ---- the key-tile loop.  The wait before each barrier leaves this wave's
+    // newest copies (tile kt+2: 13 or 14 instructions) in flight and drains the
+    // older ones (tile kt+1) and all LDS traffic.  The barrier is the bare
+    // s_barrier: a workgroup fence would also drain the newest copies.
     wait_vmem();
     __syncthreads();
     int kt = kt_lo;
+    int cur = 0;                      // ring slot of tile kt
     while (kt <= kt_hi) {
-        bool restart = false;
-#pragma unroll
-        for (int half = 0; half < 2 && kt <= kt_hi; ++half, ++kt) {
-            const __bf16 *ks = half == 0 ? Ks0 : Ks1;
-            const __bf16 *vs = half == 0 ? Vs0 : Vs1;
-            if (kt < kt_hi) {
-                if (half == 0) issue_tile(kt + 1, Ks1, Vs1);
-                else issue_tile(kt + 1, Ks0, Vs0);
-            }
-            compute_tile(kt, ks, vs);
-            if (wave_restart && lane == 0) restart_flag = 1;
+        const bool ahead = kt + 2 <= kt_hi;
+        compute_tile(kt, Kring[cur], Vring[cur]);
+        const int nxt2 = cur == 0 ? 2 : cur - 1;       // slot of tile kt+2 (= slot of kt-1)
+        if (ahead) issue_tile(kt + 2, Kring[nxt2], Vring[nxt2]);
+        if (wave_restart && lane == 0) restart_flag = 1;
+        // tile kt+1 must have landed; tile kt+2's copies may stay in flight
+        if (ahead) __builtin_amdgcn_s_waitcnt(0x007D);   // vmcnt(13) lgkmcnt(0)
+        else __builtin_amdgcn_s_waitcnt(0x0070);         // vmcnt(0) lgkmcnt(0)
+        asm volatile("" ::: "memory");                   // no compiler motion across
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        if (__builtin_amdgcn_readfirstlane(restart_flag)) {
             wait_vmem();
-            __syncthreads();
-            if (__builtin_amdgcn_readfirstlane(restart_flag)) {
-                restart = true;
-                break;
-            }
-        }
-        if (restart) {
-            // some row met a key far above its reference: redo the pass from the
-            // first tile with the raised references (accumulators start from zero)
             __syncthreads();                       // every wave has read the flag
             if (tid == 0) restart_flag = 0;
 #pragma unroll
@@ -366,10 +360,15 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_kernel(PrefillParams p)
             }
             wave_restart = false;
             kt = kt_lo;
-            issue_tile(kt_lo, Ks0, Vs0);
+            cur = 0;
+            issue_tile(kt_lo, Kring[0], Vring[0]);
+            if (kt_lo + 1 <= kt_hi) issue_tile(kt_lo + 1, Kring[1], Vring[1]);
             wait_vmem();
             __syncthreads();
+            continue;
         }
+        ++kt;
+        cur = cur == 2 ? 0 : cur + 1;
     }
 
     // ---- epilogue: normalise, differential combine, gate, bf16 store
