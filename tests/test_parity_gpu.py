@@ -156,6 +156,25 @@ def test_pf_swa_32k_sampled():
             oracle_prefill_rows(x, w.window, rb, rt), "pf_swa_32k rows=%d" % len(rb))
 
 
+@pytest.mark.parametrize("window,dist", [(128, "cfg"), (128, "sharp"), (1, "sharp"), (64, "sharp"),
+                                         (129, "sharper")])
+def test_prefill_window_runs_sampled(window, dist):
+    """B=1, T=16384, 16 KV heads: enough query tiles that a workgroup walks a
+    run of 8 consecutive query tiles; whole runs (incl. their boundaries) and
+    random rows are compared."""
+    kw = {"cfg": {}, "sharp": SHARP, "sharper": SHARPER}[dist]
+    w = W.Workload("runs", "prefill", B=1, T=16384, n_kv=16, window=window)
+    log("prefill window runs W=%d dist=%s" % (window, dist))
+    x = W.prefill_inputs(w, seed=window, device="cuda", **kw)
+    out = gpu_prefill(x, window)
+    rt = np.concatenate([np.arange(0, 24 * 64), np.arange(120 * 64, 136 * 64), np.arange(16384 - 200, 16384),
+                         np.random.default_rng(window).integers(0, 16384, 256)]).astype(np.int32)
+    rt = np.unique(rt)
+    rb = np.zeros_like(rt)
+    compare(out[torch.as_tensor(rb).long(), torch.as_tensor(rt).long()],
+            oracle_prefill_rows(x, window, rb, rt), "runs W%d %s rows=%d" % (window, dist, len(rt)))
+
+
 # ---------------------------------------------------------------------------
 # decode
 # ---------------------------------------------------------------------------
