@@ -60,19 +60,33 @@ constexpr int K_TILE_COPIES = PF_BN / K_ROWS_PER_COPY;                          
 constexpr int V_TILE_COPIES = (PF_BN + V_ROWS_PER_COPY - 1) / V_ROWS_PER_COPY;  // 22
 static_assert(K_ROWS_PER_COPY * KS_CHUNKS <= 64 && V_ROWS_PER_COPY * VS_CHUNKS <= 64, "rows per copy");
 
-typedef __attribute__((address_space(3))) void lds_void_t;
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
 
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
 // Buffer resource over `bytes` bytes from `base` (raw, no stride): reads at
 // byte offsets >= bytes return zeros.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, 0x00020000);
+__device__ __forceinline__ i32x4 make_rsrc(const void *base, uint32_t bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    return i32x4{(int)(uint32_t)a, (int)(uint32_t)(a >> 32), (int)bytes, 0x00020000};
 }
 
-// One 16-byte buffer -> LDS copy per lane; lane l writes lds_base + 16*l.
-__device__ __forceinline__ void copy16_to_lds(__amdgpu_buffer_rsrc_t rsrc, uint32_t byte_off, __bf16 *lds_base) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t *)lds_base, 16, byte_off, 0, 0, 0);
+// LDS byte address of a shared-memory pointer, as a wave-uniform value.
+__device__ __forceinline__ uint32_t lds_addr(const __bf16 *p) {
+    const uint32_t a = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) __bf16 *)p;
+    return __builtin_amdgcn_readfirstlane(a);
+}
+
+// One 16-byte buffer -> LDS copy per lane; lane l writes lds_base + 16*l
+// (lds_base goes to M0).  Written as a statement the compiler does not model
+// as an LDS write: otherwise it would drain every copy in flight before each
+// later LDS read it cannot prove disjoint from the copy (the ring slot is a
+// run-time index).  The kernel itself orders the copies against the reads:
+// s_waitcnt vmcnt(N) and a barrier before a tile is read.
+__device__ __forceinline__ void copy16_to_lds(const i32x4 &rsrc, uint32_t byte_off, uint32_t lds_base) {
+    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                 :: "v"(byte_off), "s"(rsrc), "{m0}"(lds_base) : "memory");
 }
 
 // Wait until this wave's outstanding vector-memory loads (including the
@@ -141,8 +155,8 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_kernel(PrefillParams p)
     // as zeros (those keys are always masked).  A lane's byte offset within a
     // copy is fixed; the tile and copy add a uniform offset.
     const uint32_t krow_b = (uint32_t)n_kv * D_QK * 2, vrow_b = (uint32_t)n_kv * D_V * 2;
-    const __amdgpu_buffer_rsrc_t k_rsrc = make_rsrc(p.k + (seq0 * n_kv + j) * D_QK, (uint32_t)T * krow_b);
-    const __amdgpu_buffer_rsrc_t v_rsrc = make_rsrc(p.v + (seq0 * n_kv + j) * D_V, (uint32_t)T * vrow_b);
+    const i32x4 k_rsrc = make_rsrc(p.k + (seq0 * n_kv + j) * D_QK, (uint32_t)T * krow_b);
+    const i32x4 v_rsrc = make_rsrc(p.v + (seq0 * n_kv + j) * D_V, (uint32_t)T * vrow_b);
     const int uwave = __builtin_amdgcn_readfirstlane(wave);
     const int k_lr = lane / KS_CHUNKS, k_ch = lane % KS_CHUNKS;    // row within the copy, chunk
     const int v_lr = lane / VS_CHUNKS, v_ch = lane % VS_CHUNKS;
@@ -155,13 +169,13 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_kernel(PrefillParams p)
 #pragma unroll
         for (int c = 0; c < K_TILE_COPIES / 4; ++c) {
             const int row0 = K_ROWS_PER_COPY * (uwave + 4 * c);
-            if (k_on) copy16_to_lds(k_rsrc, k_lane + (uint32_t)(kbase + row0) * krow_b, ks + row0 * KS_ROW);
+            if (k_on) copy16_to_lds(k_rsrc, k_lane + (uint32_t)(kbase + row0) * krow_b, lds_addr(ks + row0 * KS_ROW));
         }
 #pragma unroll
         for (int c = 0; c < (V_TILE_COPIES + 3) / 4; ++c) {
             const int row0 = V_ROWS_PER_COPY * (uwave + 4 * c);
             if (row0 < PF_BN && v_on && row0 + v_lr < PF_BN)
-                copy16_to_lds(v_rsrc, v_lane + (uint32_t)(kbase + row0) * vrow_b, vs + row0 * VS_ROW);
+                copy16_to_lds(v_rsrc, v_lane + (uint32_t)(kbase + row0) * vrow_b, lds_addr(vs + row0 * VS_ROW));
         }
     };
     // Tile t may be copied into slot t % 3 once tile t-3 is no longer needed:
