@@ -35,6 +35,7 @@
 #include "gdla_launch.h"
 
 #include <algorithm>
+#include <atomic>
 
 namespace gdla {
 
@@ -63,30 +64,17 @@ static_assert(K_ROWS_PER_COPY * KS_CHUNKS <= 64 && V_ROWS_PER_COPY * VS_CHUNKS <
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
 
-typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;
 
 // Buffer resource over `bytes` bytes from `base` (raw, no stride): reads at
 // byte offsets >= bytes return zeros.
-__device__ __forceinline__ i32x4 make_rsrc(const void *base, uint32_t bytes) {
-    const uint64_t a = reinterpret_cast<uint64_t>(base);
-    return i32x4{(int)(uint32_t)a, (int)(uint32_t)(a >> 32), (int)bytes, 0x00020000};
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, 0x00020000);
 }
 
-// LDS byte address of a shared-memory pointer, as a wave-uniform value.
-__device__ __forceinline__ uint32_t lds_addr(const __bf16 *p) {
-    const uint32_t a = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) __bf16 *)p;
-    return __builtin_amdgcn_readfirstlane(a);
-}
-
-// One 16-byte buffer -> LDS copy per lane; lane l writes lds_base + 16*l
-// (lds_base goes to M0).  Written as a statement the compiler does not model
-// as an LDS write: otherwise it would drain every copy in flight before each
-// later LDS read it cannot prove disjoint from the copy (the ring slot is a
-// run-time index).  The kernel itself orders the copies against the reads:
-// s_waitcnt vmcnt(N) and a barrier before a tile is read.
-__device__ __forceinline__ void copy16_to_lds(const i32x4 &rsrc, uint32_t byte_off, uint32_t lds_base) {
-    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
-                 :: "v"(byte_off), "s"(rsrc), "{m0}"(lds_base) : "memory");
+// One 16-byte buffer -> LDS copy per lane; lane l writes lds_base + 16*l.
+__device__ __forceinline__ void copy16_to_lds(__amdgpu_buffer_rsrc_t rsrc, uint32_t byte_off, __bf16 *lds_base) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t *)lds_base, 16, byte_off, 0, 0, 0);
 }
 
 // Wait until this wave's outstanding vector-memory loads (including the
@@ -109,24 +97,32 @@ struct PrefillParams {
     int n_runs;                       // work items per sequence and KV head
 };
 
-// Work item = (head instance b*n_kv+j, a run of consecutive query tiles).
-// Consecutive workgroups go to the 8 XCDs in turn; each XCD gets a fixed
-// subset of head instances so that the K/V of a head stay in one XCD's L2.
-// Full causal layers use runs of one tile and hand out the heaviest (last)
-// query tiles first; sliding-window layers use longer runs, whose K/V tiles
-// overlap from one query tile to the next.
-__device__ __forceinline__ void map_item(int bid, int n_hi, int n_runs, int run_len, bool causal,
-                                         int &hi, int &qt_first) {
-    int rank;
-    if ((n_hi & 7) == 0) {
-        const int xcd = bid & 7, slot = bid >> 3, per_xcd = n_hi >> 3;
-        rank = slot / per_xcd;
-        hi = (slot % per_xcd) * 8 + xcd;
-    } else {
-        hi = bid % n_hi;
-        rank = bid / n_hi;
-    }
+// Work item = (head instance hi = b*n_kv + j, a run of consecutive query
+// tiles).  The kernel is persistent: one workgroup per CU walks a fixed list
+// of items, so that the next item's queries and first K/V tiles load while the
+// current item's epilogue runs, and no CU waits for a new workgroup.  Items
+// are ranked by cost (full causal: the last query tiles, the heaviest, first)
+// and dealt in snake order -- round r goes to the workgroups in ascending
+// order for even r and descending for odd r -- which evens out the work per
+// CU.  When the head instances split evenly over the 8 XCDs, the workgroups of
+// one XCD (blockIdx % 8: workgroups are spread over the XCDs in turn) deal
+// only the items of that XCD's heads, so a head's K/V stays in one L2.
+struct WorkList {
+    bool by_xcd;
+    int xcd;          // heads of this list: hi = 8m + xcd (by_xcd), else all
+    int l, n_l;       // this workgroup's place among the n_l sharing the list
+    int heads;        // head instances in the list
+    int n_items;      // items in the list
+};
+
+__device__ __forceinline__ bool work_item(const WorkList &w, int round, int n_runs, int run_len,
+                                          bool causal, int &hi, int &qt_first) {
+    const int li = round * w.n_l + ((round & 1) ? w.n_l - 1 - w.l : w.l);
+    if (li >= w.n_items) return false;
+    const int rank = li / w.heads, m = li % w.heads;
+    hi = w.by_xcd ? 8 * m + w.xcd : m;
     qt_first = (causal ? n_runs - 1 - rank : rank) * run_len;
+    return true;
 }
 
 __global__ __launch_bounds__(PF_THREADS, 1) void prefill_kernel(PrefillParams p) {
@@ -137,14 +133,23 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_kernel(PrefillParams p)
 
     const int T = p.T, n_kv = p.n_kv, window = p.window;
     const int n_sig = n_kv * GROUP;
-    int hi, qt_first;
-    map_item(blockIdx.x, p.B * n_kv, p.n_runs, p.run_len, window == 0, hi, qt_first);
-    const int b = hi / n_kv, j = hi % n_kv;
-    const int qt_end = min(qt_first + p.run_len, p.n_qt);     // one past the run's last query tile
+    const int n_hi = p.B * n_kv;
+    WorkList wl;
+    wl.by_xcd = (n_hi & 7) == 0 && (gridDim.x & 7) == 0;
+    wl.xcd = wl.by_xcd ? blockIdx.x & 7 : 0;
+    wl.l = wl.by_xcd ? blockIdx.x >> 3 : blockIdx.x;
+    wl.n_l = wl.by_xcd ? gridDim.x >> 3 : gridDim.x;
+    wl.heads = wl.by_xcd ? n_hi >> 3 : n_hi;
+    wl.n_items = p.n_runs * wl.heads;
+    const bool causal = window == 0;
+    int round = 0, hi, qt_first;
+    if (!work_item(wl, round, p.n_runs, p.run_len, causal, hi, qt_first)) return;
+    int b = hi / n_kv, j = hi % n_kv;
+    int qt_end = min(qt_first + p.run_len, p.n_qt);           // one past the run's last query tile
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int r = lane & 15, g = lane >> 4;
-    const long seq0 = (long)b * T;    // first row of sequence b
+    long seq0 = (long)b * T;          // first row of sequence b
 
     // key tiles a query tile sees: 0..t for a full causal layer, t-W+1..t with a window
     auto tile_lo = [&](int qt) { return window > 0 ? max(0, qt * PF_BM - window + 1) / PF_BN : 0; };
@@ -155,8 +160,12 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_kernel(PrefillParams p)
     // as zeros (those keys are always masked).  A lane's byte offset within a
     // copy is fixed; the tile and copy add a uniform offset.
     const uint32_t krow_b = (uint32_t)n_kv * D_QK * 2, vrow_b = (uint32_t)n_kv * D_V * 2;
-    const i32x4 k_rsrc = make_rsrc(p.k + (seq0 * n_kv + j) * D_QK, (uint32_t)T * krow_b);
-    const i32x4 v_rsrc = make_rsrc(p.v + (seq0 * n_kv + j) * D_V, (uint32_t)T * vrow_b);
+    __amdgpu_buffer_rsrc_t k_rsrc, v_rsrc;
+    auto set_rsrc = [&](long s0, int jj) {
+        k_rsrc = make_rsrc(p.k + (s0 * n_kv + jj) * D_QK, (uint32_t)T * krow_b);
+        v_rsrc = make_rsrc(p.v + (s0 * n_kv + jj) * D_V, (uint32_t)T * vrow_b);
+    };
+    set_rsrc(seq0, j);
     const int uwave = __builtin_amdgcn_readfirstlane(wave);
     const int k_lr = lane / KS_CHUNKS, k_ch = lane % KS_CHUNKS;    // row within the copy, chunk
     const int v_lr = lane / VS_CHUNKS, v_ch = lane % VS_CHUNKS;
@@ -169,20 +178,20 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_kernel(PrefillParams p)
 #pragma unroll
         for (int c = 0; c < K_TILE_COPIES / 4; ++c) {
             const int row0 = K_ROWS_PER_COPY * (uwave + 4 * c);
-            if (k_on) copy16_to_lds(k_rsrc, k_lane + (uint32_t)(kbase + row0) * krow_b, lds_addr(ks + row0 * KS_ROW));
+            if (k_on) copy16_to_lds(k_rsrc, k_lane + (uint32_t)(kbase + row0) * krow_b, ks + row0 * KS_ROW);
         }
 #pragma unroll
         for (int c = 0; c < (V_TILE_COPIES + 3) / 4; ++c) {
             const int row0 = V_ROWS_PER_COPY * (uwave + 4 * c);
             if (row0 < PF_BN && v_on && row0 + v_lr < PF_BN)
-                copy16_to_lds(v_rsrc, v_lane + (uint32_t)(kbase + row0) * vrow_b, lds_addr(vs + row0 * VS_ROW));
+                copy16_to_lds(v_rsrc, v_lane + (uint32_t)(kbase + row0) * vrow_b, vs + row0 * VS_ROW);
         }
     };
     // Tile t may be copied into slot t % 3 once tile t-3 is no longer needed:
     // at most two tiles past the tile being computed and past the lowest tile
     // any later query tile of the run still reads.  A run's query tiles see at
     // most three key tiles each (the host uses runs only when that holds).
-    const int run_last_tile = tile_hi(qt_end - 1);
+    int run_last_tile = tile_hi(qt_end - 1);
     int next_copy;                    // lowest tile not yet copied
     auto start_ring = [&](int qt) {   // first two tiles of a query tile, nothing in flight
         next_copy = tile_lo(qt);
@@ -196,11 +205,13 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_kernel(PrefillParams p)
     int tw = t0 + 16 * wave;          // first query token of this wave
     int tq = tw + r;                  // query token of this lane
     bf16x8 qf[HEADS][KK_STEPS];
-    auto load_q = [&](int qt) {       // B operand fragments, lane holds Q[tq][32kk + 8g .. +7]
+    // B operand fragments of query tile qt of the sequence starting at row s0,
+    // KV head jj: lane holds Q[tq][32kk + 8g .. +7]
+    auto load_q = [&](int qt, long s0, int jj) {
         const int t = qt * PF_BM + 16 * wave + r;
         const bool ok = t < T;
-        const __bf16 *qsrow = p.qs + ((seq0 + (ok ? t : 0)) * n_sig + GROUP * j) * D_QK + 8 * g;
-        const __bf16 *qnrow = p.qn + ((seq0 + (ok ? t : 0)) * n_kv + j) * D_QK + 8 * g;
+        const __bf16 *qsrow = p.qs + ((s0 + (ok ? t : 0)) * n_sig + GROUP * jj) * D_QK + 8 * g;
+        const __bf16 *qnrow = p.qn + ((s0 + (ok ? t : 0)) * n_kv + jj) * D_QK + 8 * g;
 #pragma unroll
         for (int kk = 0; kk < KK_STEPS; ++kk) {
 #pragma unroll
@@ -212,7 +223,7 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_kernel(PrefillParams p)
             qf[GROUP][kk] = __builtin_bit_cast(bf16x8, w);
         }
     };
-    load_q(qt_first);
+    load_q(qt_first, seq0, j);
 
     float m_ref[HEADS], l_part[HEADS];
     f32x4 o[HEADS][D_V / 16];
@@ -362,6 +373,8 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_kernel(PrefillParams p)
 
     wait_vmem();
     __syncthreads();
+    for (;;) {                        // work items of this workgroup
+    bool more_items = false;
     for (int qt = qt_first; qt < qt_end; ++qt) {
         t0 = qt * PF_BM;
         tw = t0 + 16 * wave;
@@ -428,7 +441,23 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_kernel(PrefillParams p)
                 gw[h][cb] = *reinterpret_cast<const u32x2 *>(p.gate + (row * n_sig + GROUP * j + h) * D_V +
                                                             16 * cb + 4 * g);
         const u32x2 lw = *reinterpret_cast<const u32x2 *>(p.lam + row * n_sig + GROUP * j);
-        if (qt + 1 < qt_end) load_q(qt + 1);
+        // next query tile of the run, or the first of the next work item: every
+        // wave is done with the ring, so that item's first K/V tiles are copied
+        // now, behind this epilogue, as are its queries
+        int n_b = b, n_j = j, n_qt = qt + 1;
+        if (n_qt >= qt_end) {
+            if (work_item(wl, round + 1, p.n_runs, p.run_len, causal, hi, n_qt)) {
+                more_items = true;
+                n_b = hi / n_kv;
+                n_j = hi % n_kv;
+                set_rsrc((long)n_b * T, n_j);
+                run_last_tile = tile_hi(min(n_qt + p.run_len, p.n_qt) - 1);
+                start_ring(n_qt);
+            } else {
+                n_qt = -1;
+            }
+        }
+        if (n_qt >= 0) load_q(n_qt, (long)n_b * T, n_j);
 
         float inv[HEADS];
 #pragma unroll
@@ -458,7 +487,34 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_kernel(PrefillParams p)
                 }
             }
         }
+        if (more_items) {
+            b = n_b;
+            j = n_j;
+            seq0 = (long)b * T;
+            qt_first = n_qt;
+        }
     }
+    if (!more_items) break;
+    ++round;
+    qt_end = min(qt_first + p.run_len, p.n_qt);
+    // the next item's first tiles and queries have landed in every wave
+    wait_vmem();
+    __syncthreads();
+    }
+}
+
+// Compute units of the current device (read once per device).
+static int compute_units() {
+    static std::atomic<int> cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int n = cached[dev].load(std::memory_order_relaxed);
+    if (n <= 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        cached[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
 }
 
 hipError_t launch_prefill(const void *qs, const void *qn, const void *k, const void *v,
@@ -481,13 +537,16 @@ hipError_t launch_prefill(const void *qs, const void *qn, const void *k, const v
     // Sliding windows of up to 2*PF_BN+1 keys touch at most three key tiles per
     // query tile, so a workgroup can walk a run of consecutive query tiles and
     // copy one new K/V tile per query tile; runs are sized for about two per CU.
+    const int n_cu = compute_units();
     p.run_len = 1;
     if (p.window > 0 && p.window <= 2 * PF_BN + 1) {
         const long tiles = (long)B * n_kv * p.n_qt;
-        p.run_len = (int)std::max(1L, std::min((long)p.n_qt, (tiles + 2 * 256 - 1) / (2 * 256)));
+        p.run_len = (int)std::max(1L, std::min((long)p.n_qt, (tiles + 2L * n_cu - 1) / (2L * n_cu)));
     }
     p.n_runs = (p.n_qt + p.run_len - 1) / p.run_len;
-    const long blocks = (long)B * n_kv * p.n_runs;
+    // one persistent workgroup per CU (at most one fits: LDS and registers)
+    const long items = (long)B * n_kv * p.n_runs;
+    const long blocks = std::min(items, (long)n_cu);
     hipLaunchKernelGGL(prefill_kernel, dim3((unsigned)blocks), dim3(PF_THREADS), 0, stream, p);
     return hipGetLastError();
 }

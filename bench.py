@@ -12,6 +12,7 @@ on), the CPU oracle timed on a bounded sample of the same workload, and the
 other workloads (sliding-window prefill, 128K prefill, decode) under "extra".
 
     python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--no-extra]
+                    [--extras pf_swa_32k,dec_full,...]
 """
 import argparse
 import glob
@@ -180,6 +181,9 @@ def main():
     ap.add_argument("--workload", default="pf_full_4k", choices=["pf_full_4k", "pf_swa_32k", "pf_full_128k"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
+    ap.add_argument("--extras", default="pf_swa_32k,pf_full_128k,dec_full,dec_swa",
+                    help="comma-separated extra workloads to time (a profile of one workload "
+                         "names just that one)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run one 1 GiB device copy (reference for HBM counter scaling)")
     args = ap.parse_args()
@@ -187,6 +191,11 @@ def main():
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)",
               file=sys.stderr)
         sys.exit(2)
+    wanted = [] if args.no_extra else [x for x in args.extras.split(",") if x]
+    for name in wanted:
+        if name not in ("pf_swa_32k", "pf_full_128k", "dec_full", "dec_swa"):
+            print("unknown extra workload %r" % name, file=sys.stderr)
+            sys.exit(2)
 
     import torch
     import workload as W
@@ -209,9 +218,9 @@ def main():
         del a, b
 
     extra = {}
-    if not args.no_extra:
+    if wanted:
         for name in ("pf_swa_32k", "pf_full_128k"):
-            if name == args.workload:
+            if name == args.workload or name not in wanted:
                 continue
             print("[bench] extra %s" % name, file=sys.stderr, flush=True)
             steps = 3 if name == "pf_full_128k" else 10
@@ -220,6 +229,8 @@ def main():
                            "gbs": r["gbs"], "hbm_frac": r["gbs"] / PEAK_HBM_GBS,
                            "kernel_ms": r["kernel_ms"], "steps": steps}
         for name in ("dec_full", "dec_swa"):
+            if name not in wanted:
+                continue
             print("[bench] extra %s" % name, file=sys.stderr, flush=True)
             extra[name] = bench_decode(name, 10, 2)
 
