@@ -31,17 +31,13 @@ constexpr float LOG2E = 1.4426950408889634f;
 // softmax reference is only raised when a new score exceeds it by more than
 // this, so unnormalised weights stay below 2^8 and fp32 cannot overflow.
 constexpr float RESCALE_LOG2 = 8.0f;
-// Prefill keeps each row's reference fixed.  A slice whose weights
-// exp2(x - ref) of one lane sum above 2^64 (so some weight exceeds 2^61)
-// restarts the pass; the restart raises every row whose maximum exceeds its
-// reference by more than 2^60 -- which includes the row that tripped the
-// check -- to that maximum plus a headroom, so slowly growing scores do not
-// restart repeatedly.  Weights thus stay below 2^64 (row sums below 2^81 for
-// 2^17 keys, far from fp32's 2^128) and the largest weight of a row stays
-// above 2^-32.
-constexpr float RESTART_SUM = 0x1p64f;
-constexpr float RAISE_LOG2 = 60.0f;
-constexpr float RESTART_HEADROOM_LOG2 = 32.0f;
+// Prefill keeps each row's reference fixed (the row's first visible maximum).
+// If one lane's part of a row sum ends a query tile above 2^62 (weights that
+// grew far past the reference) or not finite, the workgroup redoes that query
+// tile with exact row maxima as references, found by a scores-only pass; then
+// every weight is <= 1.  Below the bound, row sums stay under 2^64 and fp32
+// (max 2^128) cannot overflow for any realistic V.
+constexpr float RESTART_PART_SUM = 0x1p62f;
 
 __device__ __forceinline__ f32x4 mfma16(const bf16x8 &a, const bf16x8 &b, const f32x4 &c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -71,6 +67,12 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     const f32x2 v = {lo, hi};
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+// acc + lo + hi of a packed bf16 pair, in fp32 (one v_dot2c_f32_bf16 against (1, 1))
+__device__ __forceinline__ float sum_bf16x2(uint32_t w, float acc) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w),
+                                           __builtin_bit_cast(bf16x2, 0x3F803F80u), acc, false);
 }
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }

@@ -15,13 +15,15 @@
 //      with the gfx950 LDS transpose read (ds_read_b64_tr_b16);
 //   3. S^T = K Q^T on the matrix cores (bf16 in, fp32 out), causal / window
 //      mask on the tiles that straddle the band edge only;
-//   4. online softmax in base 2 with the scale folded in and row sums kept
-//      per lane.  Each row's reference maximum is fixed by the first visible
-//      keys it meets (the row maximum is not computed after that); later
-//      weights may grow to ~2^61 before the workgroup restarts its pass with
-//      a raised reference (rare: it needs a logit jump of ~42 in natural
-//      units).  The accumulators are thus never rescaled inside the loop,
-//      which keeps them in the matrix-core register file;
+//   4. online softmax in base 2 with the scale folded in.  Each row's
+//      reference maximum is fixed by the first visible keys it meets (the
+//      row maximum is not tracked after that), so the accumulators are never
+//      rescaled inside the loop and stay in the matrix-core register file.
+//      Row sums are taken over the same bf16-rounded weights that enter P*V.
+//      If a row's sum ends a query tile far above its reference range (logits
+//      that grew by more than ~40 natural units; rare), the workgroup redoes
+//      that query tile: a scores-only pass finds the exact row maxima, then
+//      the normal pass runs with those as references;
 //   5. O^T += V^T P^T on the matrix cores;
 //   6. epilogue in registers: H = O / l, D = H_S - lambda * H_N (each noise
 //      row repeated to its 4 signal heads), out = gate * D, rounded to bf16
@@ -129,7 +131,7 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_kernel(PrefillParams p)
     // ring of three K and three V tile slots: key tile t lives in slot t % 3
     __shared__ __attribute__((aligned(16))) __bf16 Kring[3][PF_BN * KS_ROW];
     __shared__ __attribute__((aligned(16))) __bf16 Vring[3][PF_BN * VS_ROW];
-    __shared__ int restart_flag;
+    __shared__ int restart_flag[2];   // restart requests, by parity of the query tiles done
 
     const int T = p.T, n_kv = p.n_kv, window = p.window;
     const int n_sig = n_kv * GROUP;
@@ -225,11 +227,15 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_kernel(PrefillParams p)
     };
     load_q(qt_first, seq0, j);
 
+    // l_part[h]: this lane's part of each row sum, over the bf16-rounded
+    // weights that also enter P*V (so numerator and denominator agree)
     float m_ref[HEADS], l_part[HEADS];
     f32x4 o[HEADS][D_V / 16];
     const float c_log2 = p.scale_log2;
-    if (tid == 0) restart_flag = 0;
-    bool wave_restart = false;        // this wave met a weight beyond the reference range
+    if (tid < 2) restart_flag[tid] = 0;
+    bool wave_restart = false;        // a row sum of this wave left the reference range
+    bool max_pass = false;            // scores only: exact row maxima become the references
+    int n_done = 0;                   // query tiles finished by the workgroup
 
     // ---- one key tile: 2 slices of 32 keys, each S^T = K Q^T, softmax, O^T += V^T P^T
     auto compute_tile = [&](int kt, const __bf16 *ks, const __bf16 *vs) {
@@ -239,31 +245,27 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_kernel(PrefillParams p)
         for (int sub = 0; sub < 2; ++sub) {
             const int kb0 = kt * PF_BN + 32 * sub;     // first key of this 32-key slice
             // wave-uniform skips: no valid query, all keys in the future, all keys too old
-            if (wave_restart || tw >= T || kb0 > tw + 15) continue;
+            if (tw >= T || kb0 > tw + 15) continue;
             if (window > 0 && kb0 + 31 < tw - window + 1) continue;
             const bool need_mask = (kb0 + 31 > tw) || (window > 0 && kb0 < tw + 16 - window);
 
-            // S^T = K Q^T, first the 16 keys of block 0 for all heads, then block 1,
-            // so that block 0's weights can be formed while block 1 is multiplied.
-            // K fragments are read one k-step ahead.
+            // S^T = K Q^T, first the 16 keys of block 0 for all heads, then block 1.
+            // The six K fragments of a block are read before its MFMAs.
             const __bf16 *krd = ks + (32 * sub + r) * KS_ROW + 8 * g;
             f32x4 s[HEADS][2];
             const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
             auto qk_block = [&](int kb) {
                 const __bf16 *kr = krd + 16 * kb * KS_ROW;
-                bf16x8 ka = *reinterpret_cast<const bf16x8 *>(kr);
+                bf16x8 kf[KK_STEPS];
 #pragma unroll
-                for (int kk = 0; kk < KK_STEPS; ++kk) {
-                    bf16x8 na = ka;
-                    if (kk + 1 < KK_STEPS) na = *reinterpret_cast<const bf16x8 *>(kr + 32 * (kk + 1));
+                for (int kk = 0; kk < KK_STEPS; ++kk) kf[kk] = *reinterpret_cast<const bf16x8 *>(kr + 32 * kk);
+#pragma unroll
+                for (int kk = 0; kk < KK_STEPS; ++kk)
 #pragma unroll
                     for (int h = 0; h < HEADS; ++h)
-                        s[h][kb] = mfma16(ka, qf[h][kk], kk == 0 ? zero4 : s[h][kb]);
-                    ka = na;
-                }
+                        s[h][kb] = mfma16(kf[kk], qf[h][kk], kk == 0 ? zero4 : s[h][kb]);
             };
             // weights of key block kb against the fixed references: p = 2^(x*c - ref)
-            float ps[HEADS];
             uint32_t pw[HEADS][4];
             auto weights = [&](int kb, unsigned vis) {
 #pragma unroll
@@ -275,8 +277,6 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_kernel(PrefillParams p)
                         pv[e] = fast_exp2(fmaf(s[h][kb][e], c_log2, -mref));
                         pv[e] = (vis >> (4 * kb + e)) & 1 ? pv[e] : 0.f;
                     }
-                    const float part = (pv[0] + pv[1]) + (pv[2] + pv[3]);
-                    ps[h] = kb == 0 ? part : ps[h] + part;
                     pw[h][2 * kb] = pack_bf16x2(pv[0], pv[1]);
                     pw[h][2 * kb + 1] = pack_bf16x2(pv[2], pv[3]);
                 }
@@ -304,7 +304,7 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_kernel(PrefillParams p)
             bool unset = false;
 #pragma unroll
             for (int h = 0; h < HEADS; ++h) unset |= m_ref[h] == -INFINITY;
-            if (!need_mask && !__any(unset)) {
+            if (!need_mask && !__any(unset) && !max_pass) {
                 // common case: every key visible, every reference set; one basic
                 // block, so block 0's exponentials overlap block 1's MFMAs
                 qk_block(0);
@@ -312,40 +312,28 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_kernel(PrefillParams p)
                 qk_block(1);
                 weights(1, 0xffu);
             } else {
-                // band edge or rows without a reference yet
+                // band edge, rows without a reference yet, or the scores-only pass
                 qk_block(0);
                 qk_block(1);
 #pragma unroll
                 for (int h = 0; h < HEADS; ++h) {
-                    if (__any(m_ref[h] == -INFINITY)) {
+                    if (max_pass || __any(m_ref[h] == -INFINITY)) {
                         const float mx = row_max(h);
-                        if (m_ref[h] == -INFINITY) m_ref[h] = mx;
+                        if (max_pass || m_ref[h] == -INFINITY) m_ref[h] = fmaxf(m_ref[h], mx);
                     }
                 }
+                if (max_pass) continue;
                 weights(0, vis);
                 weights(1, vis);
             }
 
-            bool jump = false;
-#pragma unroll
-            for (int h = 0; h < HEADS; ++h) jump |= ps[h] > RESTART_SUM;
-            if (__any(jump)) {
-                // a weight beyond 2^61: raise the reference of every row whose
-                // visible maximum is more than 2^60 above it, and redo the pass
-#pragma unroll
-                for (int h = 0; h < HEADS; ++h) {
-                    const float mx = row_max(h);
-                    if (mx > m_ref[h] + RAISE_LOG2) m_ref[h] = mx + RESTART_HEADROOM_LOG2;
-                }
-                wave_restart = true;
-                continue;
-            }
             bf16x8 pb[HEADS];
 #pragma unroll
             for (int h = 0; h < HEADS; ++h) {
-                l_part[h] += ps[h];
                 const u32x4 w = {pw[h][0], pw[h][1], pw[h][2], pw[h][3]};
                 pb[h] = __builtin_bit_cast(bf16x8, w);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) l_part[h] = sum_bf16x2(pw[h][i], l_part[h]);
             }
 
             // O^T += V^T P^T.  The A operand (16 columns c x 32 keys) comes from
@@ -394,30 +382,46 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_kernel(PrefillParams p)
         // copies) in flight when the tile computed next is older than it.  The
         // barrier is the bare s_barrier: a workgroup fence would also drain the
         // newest copies.
+        // The weights are taken against references fixed by each row's first
+        // visible keys.  If a lane's part of a row sum ends above 2^62 (or is
+        // not finite), the workgroup redoes the query tile in two passes: scores
+        // only, for the exact row maxima, then the normal pass with those as
+        // references (every weight <= 1, so no sum comes near 2^62).
+        bool exact = false;           // references are exact maxima: no further check
         int kt = kt_lo;
         while (kt <= kt_hi) {
             compute_tile(kt, Kring[kt % 3], Vring[kt % 3]);
-            const int nt = kt < kt_hi ? kt + 1 : next_lo;    // tile computed next
+            const bool last = kt == kt_hi;
+            if (last && !max_pass && !exact && tq < T) {
+#pragma unroll
+                for (int h = 0; h < HEADS; ++h) wave_restart |= !(l_part[h] <= RESTART_PART_SUM);
+            }
+            const int nt = !last ? kt + 1 : next_lo;    // tile computed next
             const int limit = min(min(kt, nt) + 2, run_last_tile);
             while (next_copy <= limit) issue_tile(next_copy++);
-            if (wave_restart && lane == 0) restart_flag = 1;
+            if (last && __any(wave_restart) && lane == 0) restart_flag[n_done & 1] = 1;
             if (next_copy - 1 > nt) __builtin_amdgcn_s_waitcnt(0x007D);   // vmcnt(13) lgkmcnt(0)
             else __builtin_amdgcn_s_waitcnt(0x0070);                      // vmcnt(0) lgkmcnt(0)
             asm volatile("" ::: "memory");                                // no compiler motion across
             __builtin_amdgcn_s_barrier();
             asm volatile("" ::: "memory");
-            if (__builtin_amdgcn_readfirstlane(restart_flag)) {
-                // some row met a weight far above its reference: redo this query
-                // tile from its first key tile with the raised references
+            if (last && (max_pass || (!exact && __builtin_amdgcn_readfirstlane(restart_flag[n_done & 1])))) {
+                // start the scores-only pass, or the normal pass after it
                 wait_vmem();
                 __syncthreads();                   // every wave has read the flag
-                if (tid == 0) restart_flag = 0;
+                if (tid == 0) restart_flag[n_done & 1] = 0;
+                if (!max_pass) {
+#pragma unroll
+                    for (int h = 0; h < HEADS; ++h) m_ref[h] = -INFINITY;
+                }
 #pragma unroll
                 for (int h = 0; h < HEADS; ++h) {
                     l_part[h] = 0.f;
 #pragma unroll
                     for (int cb = 0; cb < D_V / 16; ++cb) o[h][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
                 }
+                exact = max_pass;
+                max_pass = !max_pass;
                 wave_restart = false;
                 start_ring(qt);
                 wait_vmem();
@@ -427,6 +431,7 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_kernel(PrefillParams p)
             }
             ++kt;
         }
+        ++n_done;
 
         // ---- epilogue: normalise, differential combine, gate, bf16 store.  The
         // gate and lambda of this tile are requested first, then the next query
