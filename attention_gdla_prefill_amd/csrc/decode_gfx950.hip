@@ -47,18 +47,34 @@ __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// gate and lambda of column c of the 4 signal heads of group (b, j)
+struct GateCol {
+    __bf16 gate[GROUP], lam[GROUP];
+};
+
+__device__ __forceinline__ GateCol load_gate_col(const DecodeParams &p, int b, int j, int c) {
+    GateCol gc;
+    const int n_sig = p.n_kv * GROUP;
+#pragma unroll
+    for (int h = 0; h < GROUP; ++h) {
+        const long hrow = (long)b * n_sig + GROUP * j + h;
+        gc.lam[h] = p.lam[hrow];
+        gc.gate[h] = p.gate[hrow * D_V + c];
+    }
+    return gc;
+}
+
 // out[b, 4j+h, c] = gate * (A_h / L_h - lambda_h * A_n / L_n) for h = 0..3
 __device__ __forceinline__ void decode_epilogue(const DecodeParams &p, int b, int j, int c,
-                                                const float A[HEADS], const float L[HEADS]) {
+                                                const GateCol &gc, const float A[HEADS],
+                                                const float L[HEADS]) {
     const int n_sig = p.n_kv * GROUP;
     const float hn = L[GROUP] > 0.f ? A[GROUP] / L[GROUP] : 0.f;
 #pragma unroll
     for (int h = 0; h < GROUP; ++h) {
         const long hrow = (long)b * n_sig + GROUP * j + h;
         const float hs = L[h] > 0.f ? A[h] / L[h] : 0.f;
-        const float lam = (float)p.lam[hrow];
-        const float gate = (float)p.gate[hrow * D_V + c];
-        p.out[hrow * D_V + c] = (__bf16)(gate * fmaf(-lam, hn, hs));
+        p.out[hrow * D_V + c] = (__bf16)((float)gc.gate[h] * fmaf(-(float)gc.lam[h], hn, hs));
     }
 }
 
@@ -72,6 +88,9 @@ __global__ __launch_bounds__(DC_THREADS) void decode_split_kernel(DecodeParams p
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int r = lane & 15, g = lane >> 4;
 
+    // with one split the epilogue runs here: its gate and lambda load first
+    GateCol gc{};
+    if (p.n_split == 1 && tid < D_V) gc = load_gate_col(p, b, j, tid);
     const int start = p.cu[b];
     const int L = p.cu[b + 1] - start;
     const int vis_lo = p.window > 0 ? max(0, L - p.window) : 0;
@@ -215,7 +234,7 @@ __global__ __launch_bounds__(DC_THREADS) void decode_split_kernel(DecodeParams p
         A[h] = acc;
     }
     if (p.n_split == 1) {
-        decode_epilogue(p, b, j, c, A, Ls);
+        decode_epilogue(p, b, j, c, gc, A, Ls);
         return;
     }
     float *part = p.ws + (((long)b * n_kv + j) * p.n_split + sp) * PART_FLOATS;
@@ -245,7 +264,7 @@ __global__ __launch_bounds__(D_V) void decode_combine_kernel(DecodeParams p) {
         Ls[h] = l;
         A[h] = acc;
     }
-    decode_epilogue(p, b, j, c, A, Ls);
+    decode_epilogue(p, b, j, c, load_gate_col(p, b, j, c), A, Ls);
 }
 
 int decode_splits(int max_seqlen_k, int window) {
