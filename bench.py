@@ -173,6 +173,42 @@ def bench_decode(name, steps, warmup):
             "cache": "cold (512 MB buffer rewritten before each launch)"}
 
 
+def measured_peaks():
+    """Achievable rates on this GPU for context: a library bf16 GEMM and a copy."""
+    import torch
+    g = torch.Generator(device="cuda").manual_seed(0)
+    n = 8192
+    a = torch.randn(n, n, device="cuda", generator=g).bfloat16()
+    b = torch.randn(n, n, device="cuda", generator=g).bfloat16()
+    for _ in range(5):
+        torch.matmul(a, b)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 20
+    e0.record()
+    for _ in range(reps):
+        torch.matmul(a, b)
+    e1.record()
+    torch.cuda.synchronize()
+    gemm_tflops = 2 * n ** 3 * reps / (e0.elapsed_time(e1) * 1e-3) / 1e12
+    del a, b
+    src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(10):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    copy_gbs = 2 * (1 << 30) * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"bf16_gemm_8192_tflops": gemm_tflops, "bf16_gemm_frac_of_peak": gemm_tflops / PEAK_BF16_TFLOPS,
+            "copy_1gib_gbs": copy_gbs, "copy_frac_of_peak": copy_gbs / PEAK_HBM_GBS}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -188,6 +224,9 @@ def main():
                          "names just that one)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run one 1 GiB device copy (reference for HBM counter scaling)")
+    ap.add_argument("--peaks", action="store_true",
+                    help="also time a bf16 8192^3 GEMM (hipBLASLt via torch) and a 1 GiB device "
+                         "copy: achievable-rate references, reported under 'peaks'")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)",
@@ -236,6 +275,8 @@ def main():
             print("[bench] extra %s" % name, file=sys.stderr, flush=True)
             extra[name] = bench_decode(name, 10, 2)
 
+    peaks = measured_peaks() if args.peaks else None
+
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline", file=sys.stderr, flush=True)
@@ -267,6 +308,8 @@ def main():
         "cpu_baseline": cpu,
         "extra": extra,
     }
+    if peaks is not None:
+        line["peaks"] = peaks
     print(json.dumps(line), flush=True)
 
 
