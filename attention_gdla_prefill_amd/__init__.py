@@ -3,5 +3,5 @@
 The computation lives in hand-written HIP kernels behind the C ABI of
 include/gdla.h (libgdla.so); this package is its Python binding.
 """
-from .api import decode, decode_workspace_size, prefill  # noqa: F401
+from .api import decode, decode_workspace_size, prefill, prefill_prefix  # noqa: F401
 from ._lib import GdlaError  # noqa: F401

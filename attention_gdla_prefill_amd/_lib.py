@@ -17,6 +17,8 @@ SIGNATURES = {
     "gdla_last_error": (ctypes.c_char_p, []),
     "gdla_prefill": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I,
                           ctypes.c_float, _P]),
+    "gdla_prefill_prefix": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I,
+                                 ctypes.c_float, _P]),
     "gdla_decode_workspace_size": (ctypes.c_size_t, [_I, _I, _I, _I]),
     "gdla_decode": (_I, [_P, _P, _P, _P, _P, _I, _P, _P, _P, _P, ctypes.c_size_t,
                          _I, _I, _I, _I, _I, _I, ctypes.c_float, _P]),

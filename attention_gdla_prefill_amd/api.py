@@ -60,6 +60,39 @@ def prefill(q_signal, q_noise, k, v, lam, gate, window=0, scale=None, out=None):
     return out
 
 
+def prefill_prefix(q_signal, q_noise, k, v, lam, gate, window=0, scale=None, out=None):
+    """The attention core for T_q new tokens after a prefix already in K/V.
+
+    q_signal [B,T_q,4*n_kv,192], q_noise [B,T_q,n_kv,192], lam [B,T_q,4*n_kv],
+    gate [B,T_q,4*n_kv,128]; k [B,P+T_q,n_kv,192] and v [B,P+T_q,n_kv,128]
+    hold the P prefix rows first.  Query row i sits at position P + i.
+    Returns out [B,T_q,4*n_kv,128] bf16, enqueued on the current stream.
+    """
+    B, Tk, n_kv, d_qk = k.shape
+    Tq = q_signal.shape[1]
+    P = Tk - Tq
+    if P < 0:
+        raise ValueError("k has %d rows per sequence, fewer than the %d queries" % (Tk, Tq))
+    n_sig = n_kv * GROUP
+    _check(q_signal, "q_signal", (B, Tq, n_sig, D_QK))
+    _check(q_noise, "q_noise", (B, Tq, n_kv, D_QK))
+    _check(k, "k", (B, Tk, n_kv, D_QK))
+    _check(v, "v", (B, Tk, n_kv, D_V))
+    _check(lam, "lam", (B, Tq, n_sig))
+    _check(gate, "gate", (B, Tq, n_sig, D_V))
+    if out is None:
+        out = torch.empty((B, Tq, n_sig, D_V), dtype=torch.bfloat16, device=k.device)
+    _check(out, "out", (B, Tq, n_sig, D_V))
+    if scale is None:
+        scale = 1.0 / math.sqrt(D_QK)
+    lib = _lib.load()
+    _lib.check(lib.gdla_prefill_prefix(
+        q_signal.data_ptr(), q_noise.data_ptr(), k.data_ptr(), v.data_ptr(), lam.data_ptr(),
+        gate.data_ptr(), out.data_ptr(), B, Tq, P, n_kv, GROUP, D_QK, D_V, int(window),
+        float(scale), _stream_ptr(k.device)))
+    return out
+
+
 def decode_workspace_size(B, n_kv, max_seqlen_k, window=0):
     return int(_lib.load().gdla_decode_workspace_size(B, n_kv, max_seqlen_k, int(window)))
 

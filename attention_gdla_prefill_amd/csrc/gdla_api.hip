@@ -64,15 +64,16 @@ extern "C" const char *gdla_status_string(int status) {
 
 extern "C" const char *gdla_last_error(void) { return g_last_error; }
 
-extern "C" int gdla_prefill(const void *q_signal, const void *q_noise, const void *k, const void *v,
-                            const void *lambda_, const void *gate, void *out, int B, int T, int n_kv,
-                            int group, int d_qk, int d_v, int window, float softmax_scale,
-                            void *stream) {
+extern "C" int gdla_prefill_prefix(const void *q_signal, const void *q_noise, const void *k,
+                                   const void *v, const void *lambda_, const void *gate, void *out,
+                                   int B, int T_q, int P, int n_kv, int group, int d_qk, int d_v,
+                                   int window, float softmax_scale, void *stream) {
     g_last_error[0] = 0;
-    if (B < 0 || T < 0) return fail(GDLA_ERR_INVALID_ARG, "B and T must be >= 0 (got %d, %d)", B, T);
+    if (B < 0 || T_q < 0 || P < 0)
+        return fail(GDLA_ERR_INVALID_ARG, "B, T_q and P must be >= 0 (got %d, %d, %d)", B, T_q, P);
     if (int rc = check_head_shape(n_kv, group, d_qk, d_v)) return rc;
     if (int rc = check_scale_window(softmax_scale, window)) return rc;
-    if (B == 0 || T == 0) return GDLA_OK;
+    if (B == 0 || T_q == 0) return GDLA_OK;
 
     const void *ptrs[7] = {q_signal, q_noise, k, v, lambda_, gate, out};
     const char *names[7] = {"q_signal", "q_noise", "k", "v", "lambda", "gate", "out"};
@@ -80,32 +81,47 @@ extern "C" int gdla_prefill(const void *q_signal, const void *q_noise, const voi
         if (!ptrs[i]) return fail(GDLA_ERR_INVALID_ARG, "%s is NULL", names[i]);
         if (!aligned(ptrs[i], 16)) return fail(GDLA_ERR_MISALIGNED, "%s is not 16-byte aligned", names[i]);
     }
-    const long double rows = (long double)B * T;
+    const long double Tk = (long double)P + T_q;
     const long double n_sig = (long double)n_kv * group;
-    if (rows * n_sig * d_qk * 2 >= 4.6e18L)
+    if ((long double)B * Tk * n_sig * d_qk * 2 >= 4.6e18L)
         return fail(GDLA_ERR_INVALID_ARG, "tensor sizes exceed the 2^62-byte limit");
-    if (gdla::prefill_grid_blocks(B, T, n_kv) >= (1L << 31))
-        return fail(GDLA_ERR_INVALID_ARG, "B * n_kv * ceil(T/64) must be < 2^31");
-    if ((long double)(T + 64) * n_kv * d_qk * 2 >= 2147483648.0L)
-        return fail(GDLA_ERR_UNSUPPORTED, "one sequence's K rows must span < 2^31 bytes ((T+64)*n_kv*d_qk*2)");
+    if (Tk >= 2147483647.0L - 64) return fail(GDLA_ERR_INVALID_ARG, "P + T_q must be < 2^31 - 64");
+    if (gdla::prefill_grid_blocks(B, T_q, P, n_kv) >= (1L << 31))
+        return fail(GDLA_ERR_INVALID_ARG, "B * n_kv * (query tiles) must be < 2^31");
+    if ((Tk + 64) * n_kv * d_qk * 2 >= 2147483648.0L)
+        return fail(GDLA_ERR_UNSUPPORTED,
+                    "one sequence's K rows must span < 2^31 bytes ((P+T_q+64)*n_kv*d_qk*2)");
 
-    const uintptr_t r = (uintptr_t)B * (uintptr_t)T;
+    const uintptr_t rq = (uintptr_t)B * (uintptr_t)T_q;
+    const uintptr_t rk = (uintptr_t)B * ((uintptr_t)P + (uintptr_t)T_q);
     const uintptr_t ns = (uintptr_t)n_kv * group;
     const Range in[6] = {
-        {"q_signal", (uintptr_t)q_signal, (uintptr_t)q_signal + r * ns * d_qk * 2},
-        {"q_noise", (uintptr_t)q_noise, (uintptr_t)q_noise + r * n_kv * d_qk * 2},
-        {"k", (uintptr_t)k, (uintptr_t)k + r * n_kv * d_qk * 2},
-        {"v", (uintptr_t)v, (uintptr_t)v + r * n_kv * d_v * 2},
-        {"lambda", (uintptr_t)lambda_, (uintptr_t)lambda_ + r * ns * 2},
-        {"gate", (uintptr_t)gate, (uintptr_t)gate + r * ns * d_v * 2}};
-    const Range o = {"out", (uintptr_t)out, (uintptr_t)out + r * ns * d_v * 2};
+        {"q_signal", (uintptr_t)q_signal, (uintptr_t)q_signal + rq * ns * d_qk * 2},
+        {"q_noise", (uintptr_t)q_noise, (uintptr_t)q_noise + rq * n_kv * d_qk * 2},
+        {"k", (uintptr_t)k, (uintptr_t)k + rk * n_kv * d_qk * 2},
+        {"v", (uintptr_t)v, (uintptr_t)v + rk * n_kv * d_v * 2},
+        {"lambda", (uintptr_t)lambda_, (uintptr_t)lambda_ + rq * ns * 2},
+        {"gate", (uintptr_t)gate, (uintptr_t)gate + rq * ns * d_v * 2}};
+    const Range o = {"out", (uintptr_t)out, (uintptr_t)out + rq * ns * d_v * 2};
     for (const Range &x : in)
         if (overlaps(o, x)) return fail(GDLA_ERR_INVALID_ARG, "out overlaps %s", x.name);
 
-    hipError_t e = gdla::launch_prefill(q_signal, q_noise, k, v, lambda_, gate, out, B, T, n_kv,
+    hipError_t e = gdla::launch_prefill(q_signal, q_noise, k, v, lambda_, gate, out, B, T_q, P, n_kv,
                                         window, softmax_scale, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(GDLA_ERR_HIP, "prefill launch: %s", hipGetErrorString(e));
     return GDLA_OK;
+}
+
+extern "C" int gdla_prefill(const void *q_signal, const void *q_noise, const void *k, const void *v,
+                            const void *lambda_, const void *gate, void *out, int B, int T, int n_kv,
+                            int group, int d_qk, int d_v, int window, float softmax_scale,
+                            void *stream) {
+    if (T < 0) {
+        g_last_error[0] = 0;
+        return fail(GDLA_ERR_INVALID_ARG, "B and T must be >= 0 (got %d, %d)", B, T);
+    }
+    return gdla_prefill_prefix(q_signal, q_noise, k, v, lambda_, gate, out, B, T, 0, n_kv, group,
+                               d_qk, d_v, window, softmax_scale, stream);
 }
 
 extern "C" size_t gdla_decode_workspace_size(int B, int n_kv, int max_seqlen_k, int window) {

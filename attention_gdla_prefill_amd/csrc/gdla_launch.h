@@ -9,10 +9,12 @@
 
 namespace gdla {
 
+// Prefill of Tq query rows per sequence at positions P .. P+Tq-1 over P+Tq key rows.
 hipError_t launch_prefill(const void *qs, const void *qn, const void *k, const void *v,
-                          const void *lam, const void *gate, void *out, int B, int T, int n_kv,
+                          const void *lam, const void *gate, void *out, int B, int Tq, int P, int n_kv,
                           int window, float scale, hipStream_t stream);
-long prefill_grid_blocks(int B, int T, int n_kv);
+// Query tiles of one (sequence, KV head) times B * n_kv.
+long prefill_grid_blocks(int B, int Tq, int P, int n_kv);
 
 // Number of cache splits (workgroups per (sequence, KV head)) for decode.
 int decode_splits(int max_seqlen_k, int window);

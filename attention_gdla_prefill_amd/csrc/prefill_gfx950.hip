@@ -92,7 +92,9 @@ __device__ __forceinline__ s16x4 lds_read_tr16(const __bf16 *p) {
 struct PrefillParams {
     const __bf16 *qs, *qn, *k, *v, *lam, *gate;
     __bf16 *out;
-    int B, T, n_kv, window;
+    int B, n_kv, window;
+    int Tq;                           // query rows per sequence (positions P .. P+Tq-1)
+    int P;                            // keys before the first query (a prefix already in K/V)
     float scale_log2;                 // softmax scale * log2(e)
     int n_qt;                         // query tiles per sequence
     int run_len;                      // query tiles per work item
@@ -127,13 +129,20 @@ __device__ __forceinline__ bool work_item(const WorkList &w, int round, int n_ru
     return true;
 }
 
+// PREFIX: queries start after a prefix of keys (P > 0); the P = 0 instance
+// folds the position offsets away.
+template <bool PREFIX>
 __global__ __launch_bounds__(PF_THREADS, 1) void prefill_kernel(PrefillParams p) {
     // ring of three K and three V tile slots: key tile t lives in slot t % 3
     __shared__ __attribute__((aligned(16))) __bf16 Kring[3][PF_BN * KS_ROW];
     __shared__ __attribute__((aligned(16))) __bf16 Vring[3][PF_BN * VS_ROW];
     __shared__ int restart_flag[2];   // restart requests, by parity of the query tiles done
 
-    const int T = p.T, n_kv = p.n_kv, window = p.window;
+    // positions: query row i sits at P + i; every position < T holds a key.
+    // Query tiles start at q0 = P rounded down to 64 so that they line up with
+    // the key tiles; rows outside P .. T-1 are computed but never stored.
+    const int Tq = p.Tq, P = PREFIX ? p.P : 0, q0 = P / PF_BM * PF_BM, T = P + Tq;
+    const int n_kv = p.n_kv, window = p.window;
     const int n_sig = n_kv * GROUP;
     const int n_hi = p.B * n_kv;
     WorkList wl;
@@ -151,11 +160,12 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_kernel(PrefillParams p)
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int r = lane & 15, g = lane >> 4;
-    long seq0 = (long)b * T;          // first row of sequence b
+    long kseq0 = (long)b * T;         // first K/V row of sequence b
+    long qseq0 = (long)b * Tq;        // first query (and gate / lambda / out) row of sequence b
 
     // key tiles a query tile sees: 0..t for a full causal layer, t-W+1..t with a window
-    auto tile_lo = [&](int qt) { return window > 0 ? max(0, qt * PF_BM - window + 1) / PF_BN : 0; };
-    auto tile_hi = [&](int qt) { return (min(qt * PF_BM + PF_BM, T) - 1) / PF_BN; };
+    auto tile_lo = [&](int qt) { return window > 0 ? max(0, q0 + qt * PF_BM - window + 1) / PF_BN : 0; };
+    auto tile_hi = [&](int qt) { return (min(q0 + qt * PF_BM + PF_BM, T) - 1) / PF_BN; };
 
     // ---- direct HBM -> LDS copy of key tile kt through buffer resources that
     // cover this sequence's rows of KV head j: rows past the sequence end read
@@ -167,7 +177,7 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_kernel(PrefillParams p)
         k_rsrc = make_rsrc(p.k + (s0 * n_kv + jj) * D_QK, (uint32_t)T * krow_b);
         v_rsrc = make_rsrc(p.v + (s0 * n_kv + jj) * D_V, (uint32_t)T * vrow_b);
     };
-    set_rsrc(seq0, j);
+    set_rsrc(kseq0, j);
     const int uwave = __builtin_amdgcn_readfirstlane(wave);
     const int k_lr = lane / KS_CHUNKS, k_ch = lane % KS_CHUNKS;    // row within the copy, chunk
     const int v_lr = lane / VS_CHUNKS, v_ch = lane % VS_CHUNKS;
@@ -203,17 +213,18 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_kernel(PrefillParams p)
     start_ring(qt_first);
 
     // ---- per-query-tile state, reset for every query tile of the run
-    int t0 = qt_first * PF_BM;
+    int t0 = q0 + qt_first * PF_BM;
     int tw = t0 + 16 * wave;          // first query token of this wave
     int tq = tw + r;                  // query token of this lane
     bf16x8 qf[HEADS][KK_STEPS];
-    // B operand fragments of query tile qt of the sequence starting at row s0,
-    // KV head jj: lane holds Q[tq][32kk + 8g .. +7]
+    // B operand fragments of query tile qt of the sequence whose query rows
+    // start at s0, KV head jj: lane holds Q[tq][32kk + 8g .. +7]
     auto load_q = [&](int qt, long s0, int jj) {
-        const int t = qt * PF_BM + 16 * wave + r;
-        const bool ok = t < T;
-        const __bf16 *qsrow = p.qs + ((s0 + (ok ? t : 0)) * n_sig + GROUP * jj) * D_QK + 8 * g;
-        const __bf16 *qnrow = p.qn + ((s0 + (ok ? t : 0)) * n_kv + jj) * D_QK + 8 * g;
+        const int t = q0 + qt * PF_BM + 16 * wave + r;       // position
+        const bool ok = (!PREFIX || t >= P) && t < T;
+        const int qrow = ok ? (PREFIX ? t - P : t) : 0;
+        const __bf16 *qsrow = p.qs + ((s0 + qrow) * n_sig + GROUP * jj) * D_QK + 8 * g;
+        const __bf16 *qnrow = p.qn + ((s0 + qrow) * n_kv + jj) * D_QK + 8 * g;
 #pragma unroll
         for (int kk = 0; kk < KK_STEPS; ++kk) {
 #pragma unroll
@@ -225,7 +236,7 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_kernel(PrefillParams p)
             qf[GROUP][kk] = __builtin_bit_cast(bf16x8, w);
         }
     };
-    load_q(qt_first, seq0, j);
+    load_q(qt_first, qseq0, j);
 
     // l_part[h]: this lane's part of each row sum, over the bf16-rounded
     // weights that also enter P*V (so numerator and denominator agree)
@@ -245,7 +256,7 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_kernel(PrefillParams p)
         for (int sub = 0; sub < 2; ++sub) {
             const int kb0 = kt * PF_BN + 32 * sub;     // first key of this 32-key slice
             // wave-uniform skips: no valid query, all keys in the future, all keys too old
-            if (tw >= T || kb0 > tw + 15) continue;
+            if (tw >= T || (PREFIX && tw + 15 < P) || kb0 > tw + 15) continue;
             if (window > 0 && kb0 + 31 < tw - window + 1) continue;
             const bool need_mask = (kb0 + 31 > tw) || (window > 0 && kb0 < tw + 16 - window);
 
@@ -364,7 +375,7 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_kernel(PrefillParams p)
     for (;;) {                        // work items of this workgroup
     bool more_items = false;
     for (int qt = qt_first; qt < qt_end; ++qt) {
-        t0 = qt * PF_BM;
+        t0 = q0 + qt * PF_BM;
         tw = t0 + 16 * wave;
         tq = tw + r;
         const int kt_lo = tile_lo(qt), kt_hi = tile_hi(qt);
@@ -392,7 +403,7 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_kernel(PrefillParams p)
         while (kt <= kt_hi) {
             compute_tile(kt, Kring[kt % 3], Vring[kt % 3]);
             const bool last = kt == kt_hi;
-            if (last && !max_pass && !exact && tq < T) {
+            if (last && !max_pass && !exact && (!PREFIX || tq >= P) && tq < T) {
 #pragma unroll
                 for (int h = 0; h < HEADS; ++h) wave_restart |= !(l_part[h] <= RESTART_PART_SUM);
             }
@@ -436,8 +447,8 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_kernel(PrefillParams p)
         // ---- epilogue: normalise, differential combine, gate, bf16 store.  The
         // gate and lambda of this tile are requested first, then the next query
         // tile's queries, so that the epilogue does not wait behind those.
-        const bool row_ok = tq < T;
-        const long row = seq0 + (row_ok ? tq : 0);
+        const bool row_ok = (!PREFIX || tq >= P) && tq < T;
+        const long row = qseq0 + (row_ok ? (PREFIX ? tq - P : tq) : 0);
         u32x2 gw[GROUP][D_V / 16];
 #pragma unroll
         for (int cb = 0; cb < D_V / 16; ++cb)
@@ -462,7 +473,7 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_kernel(PrefillParams p)
                 n_qt = -1;
             }
         }
-        if (n_qt >= 0) load_q(n_qt, (long)n_b * T, n_j);
+        if (n_qt >= 0) load_q(n_qt, (long)n_b * Tq, n_j);
 
         float inv[HEADS];
 #pragma unroll
@@ -495,7 +506,8 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_kernel(PrefillParams p)
         if (more_items) {
             b = n_b;
             j = n_j;
-            seq0 = (long)b * T;
+            kseq0 = (long)b * T;
+            qseq0 = (long)b * Tq;
             qt_first = n_qt;
         }
     }
@@ -523,7 +535,7 @@ static int compute_units() {
 }
 
 hipError_t launch_prefill(const void *qs, const void *qn, const void *k, const void *v,
-                          const void *lam, const void *gate, void *out, int B, int T, int n_kv,
+                          const void *lam, const void *gate, void *out, int B, int Tq, int P, int n_kv,
                           int window, float scale, hipStream_t stream) {
     PrefillParams p;
     p.qs = static_cast<const __bf16 *>(qs);
@@ -534,11 +546,12 @@ hipError_t launch_prefill(const void *qs, const void *qn, const void *k, const v
     p.gate = static_cast<const __bf16 *>(gate);
     p.out = static_cast<__bf16 *>(out);
     p.B = B;
-    p.T = T;
+    p.Tq = Tq;
+    p.P = P;
     p.n_kv = n_kv;
-    p.window = window >= T ? 0 : window;     // a window covering the sequence is full causal
+    p.window = window >= P + Tq ? 0 : window;  // a window covering the sequence is full causal
     p.scale_log2 = scale * LOG2E;
-    p.n_qt = (T + PF_BM - 1) / PF_BM;
+    p.n_qt = (P % PF_BM + Tq + PF_BM - 1) / PF_BM;
     // Sliding windows of up to 2*PF_BN+1 keys touch at most three key tiles per
     // query tile, so a workgroup can walk a run of consecutive query tiles and
     // copy one new K/V tile per query tile; runs are sized for about two per CU.
@@ -552,12 +565,15 @@ hipError_t launch_prefill(const void *qs, const void *qn, const void *k, const v
     // one persistent workgroup per CU (at most one fits: LDS and registers)
     const long items = (long)B * n_kv * p.n_runs;
     const long blocks = std::min(items, (long)n_cu);
-    hipLaunchKernelGGL(prefill_kernel, dim3((unsigned)blocks), dim3(PF_THREADS), 0, stream, p);
+    if (P > 0)
+        hipLaunchKernelGGL(prefill_kernel<true>, dim3((unsigned)blocks), dim3(PF_THREADS), 0, stream, p);
+    else
+        hipLaunchKernelGGL(prefill_kernel<false>, dim3((unsigned)blocks), dim3(PF_THREADS), 0, stream, p);
     return hipGetLastError();
 }
 
-long prefill_grid_blocks(int B, int T, int n_kv) {
-    return (long)B * n_kv * ((T + PF_BM - 1) / PF_BM);
+long prefill_grid_blocks(int B, int Tq, int P, int n_kv) {
+    return (long)B * n_kv * ((P % PF_BM + (long)Tq + PF_BM - 1) / PF_BM);
 }
 
 }  // namespace gdla

@@ -33,16 +33,21 @@ FLOP_PER_PAIR = 640            # 2*192 (QK^T) + 2*128 (PV) per (query head, quer
 N_HEADS = 80                   # 64 signal + 16 noise query heads
 
 
-def pairs_prefill(B, T, window):
-    if window <= 0 or window >= T:
-        return B * T * (T + 1) // 2
-    return B * (window * (window + 1) // 2 + (T - window) * window)
+def pairs_prefill(B, T, window, prefix=0):
+    """Unmasked (query, key) pairs per head: queries at positions prefix .. T-1."""
+    def upto(n):            # sum over positions t < n of the keys t sees
+        if window <= 0 or window >= n:
+            return n * (n + 1) // 2
+        return window * (window + 1) // 2 + (n - window) * window
+    return B * (upto(T) - upto(prefix))
 
 
-def prefill_bytes(B, T, n_kv=16, n_sig=64):
-    # q_signal, q_noise, k, v, lambda, gate in; out written; each once (bf16)
-    per_tok = 2 * (n_sig * 192 + n_kv * 192 + n_kv * 192 + n_kv * 128 + n_sig + 2 * n_sig * 128)
-    return B * T * per_tok
+def prefill_bytes(B, T, n_kv=16, n_sig=64, prefix=0):
+    # q_signal, q_noise, lambda, gate in and out written for each query token;
+    # k, v in for every token (prefix included); each once, bf16
+    per_q = 2 * (n_sig * 192 + n_kv * 192 + n_sig + 2 * n_sig * 128)
+    per_kv = 2 * (n_kv * 192 + n_kv * 128)
+    return B * ((T - prefix) * per_q + T * per_kv)
 
 
 def decode_bytes(lengths, window, n_kv=16, n_sig=64):
@@ -121,14 +126,22 @@ def bench_prefill(name, steps, warmup):
     import workload as W
     w = W.WORKLOADS[name]
     x = W.prefill_inputs(w, seed=0, device="cuda")
-    out = torch.empty((w.B, w.T, w.n_sig, 128), dtype=torch.bfloat16, device="cuda")
+    P = w.prefix
     stream = torch.cuda.current_stream()
-    fn = lambda: gdla.prefill(x["q_signal"], x["q_noise"], x["k"], x["v"], x["lam"], x["gate"],
-                              window=w.window, out=out)
+    if P == 0:
+        out = torch.empty((w.B, w.T, w.n_sig, 128), dtype=torch.bfloat16, device="cuda")
+        fn = lambda: gdla.prefill(x["q_signal"], x["q_noise"], x["k"], x["v"], x["lam"], x["gate"],
+                                  window=w.window, out=out)
+    else:
+        for key in ("q_signal", "q_noise", "lam", "gate"):       # the queries: positions P .. T-1
+            x[key] = x[key][:, P:].contiguous()
+        out = torch.empty((w.B, w.T - P, w.n_sig, 128), dtype=torch.bfloat16, device="cuda")
+        fn = lambda: gdla.prefill_prefix(x["q_signal"], x["q_noise"], x["k"], x["v"], x["lam"],
+                                         x["gate"], window=w.window, out=out)
     wall, ev = time_kernel(fn, steps, warmup, stream)
     kern_ms = sum(ev) / len(ev)
-    flops = pairs_prefill(w.B, w.T, w.window) * N_HEADS * FLOP_PER_PAIR
-    nbytes = prefill_bytes(w.B, w.T)
+    flops = pairs_prefill(w.B, w.T, w.window, P) * N_HEADS * FLOP_PER_PAIR
+    nbytes = prefill_bytes(w.B, w.T, prefix=P)
     del x, out
     torch.cuda.empty_cache()
     return {"wall_ms": wall, "kernel_ms": kern_ms, "flops": flops, "bytes": nbytes,
@@ -216,10 +229,12 @@ def main():
     # warmup covers that (about 0.1 s at 4K) before 100 timed steps
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=200)
-    ap.add_argument("--workload", default="pf_full_4k", choices=["pf_full_4k", "pf_swa_32k", "pf_full_128k"])
+    ap.add_argument("--workload", default="pf_full_4k",
+                    choices=["pf_full_4k", "pf_swa_32k", "pf_full_128k", "pf_prefix_4k_32k", "pf_swa_rank"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
-    ap.add_argument("--extras", default="pf_swa_32k,pf_full_128k,dec_full,dec_swa",
+    ap.add_argument("--extras", default="pf_swa_32k,pf_full_128k,pf_prefix_4k_32k,pf_swa_rank,"
+                                        "dec_full,dec_swa",
                     help="comma-separated extra workloads to time (a profile of one workload "
                          "names just that one)")
     ap.add_argument("--copy-probe", action="store_true",
@@ -234,7 +249,8 @@ def main():
         sys.exit(2)
     wanted = [] if args.no_extra else [x for x in args.extras.split(",") if x]
     for name in wanted:
-        if name not in ("pf_swa_32k", "pf_full_128k", "dec_full", "dec_swa"):
+        if name not in ("pf_swa_32k", "pf_full_128k", "pf_prefix_4k_32k", "pf_swa_rank", "dec_full",
+                        "dec_swa"):
             print("unknown extra workload %r" % name, file=sys.stderr)
             sys.exit(2)
 
@@ -260,7 +276,7 @@ def main():
 
     extra = {}
     if wanted:
-        for name in ("pf_swa_32k", "pf_full_128k"):
+        for name in ("pf_swa_32k", "pf_full_128k", "pf_prefix_4k_32k", "pf_swa_rank"):
             if name == args.workload or name not in wanted:
                 continue
             print("[bench] extra %s" % name, file=sys.stderr, flush=True)

@@ -94,6 +94,33 @@ int gdla_prefill(const void *q_signal, const void *q_noise, const void *k, const
                  int window, float softmax_scale, void *stream);
 
 /*
+ * gdla_prefill_prefix -- the same attention core for T_q new tokens that follow
+ * a prefix of P tokens whose K and V are already there: chunked prefill, or one
+ * rank's share of a sequence-parallel layer together with the K/V rows it
+ * received from its left neighbour (the digest's window-aware context
+ * parallelism exchanges exactly the last W rows: aitrends.kr, context-parallel
+ * paragraph).  Query row i sits at position P + i.
+ *
+ *   q_signal [B, T_q, n_kv*group, d_qk]   queries of the new tokens
+ *   q_noise  [B, T_q, n_kv, d_qk]
+ *   k        [B, P + T_q, n_kv, d_qk]     rows 0 .. P-1: the prefix; P .. P+T_q-1: the new tokens
+ *   v        [B, P + T_q, n_kv, d_v]
+ *   lambda_  [B, T_q, n_kv*group]
+ *   gate     [B, T_q, n_kv*group, d_v]
+ *   out      [B, T_q, n_kv*group, d_v]   every element written; no overlap with inputs
+ *   window   0 = full causal: row i sees keys 0 .. P+i; W >= 1: keys max(0, P+i-W+1) .. P+i
+ *
+ * Row i of the result equals row P + i of gdla_prefill over the whole P + T_q
+ * tokens.  gdla_prefill(..., T, ...) is gdla_prefill_prefix(..., T, 0, ...).
+ * B = 0 or T_q = 0 is a valid empty call.  Limits as for gdla_prefill with
+ * P + T_q in place of T; P < 0 is GDLA_ERR_INVALID_ARG.
+ */
+int gdla_prefill_prefix(const void *q_signal, const void *q_noise, const void *k, const void *v,
+                        const void *lambda_, const void *gate, void *out,
+                        int B, int T_q, int P, int n_kv, int group, int d_qk, int d_v,
+                        int window, float softmax_scale, void *stream);
+
+/*
  * gdla_decode_workspace_size -- bytes of device workspace gdla_decode needs
  * for B sequences, n_kv KV heads, cached lengths up to max_seqlen_k and the
  * given window.  0 means no workspace is needed (a single pass suffices).

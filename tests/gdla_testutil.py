@@ -99,3 +99,21 @@ def oracle_decode(d, window, scale=None):
 
 def default_scale():
     return 1.0 / math.sqrt(192)
+
+
+def query_tail(x, P):
+    """The inputs of a prefix call: query-side tensors from position P on (the
+    K/V tensors keep every row)."""
+    y = dict(x)
+    for k in ("q_signal", "q_noise", "lam", "gate"):
+        y[k] = x[k][:, P:].contiguous()
+    return y
+
+
+def gpu_prefill_prefix(x, window, scale=None):
+    B, Tq, n_sig, _ = x["q_signal"].shape
+    out = torch.full((B, Tq, n_sig, 128), float("nan"), dtype=torch.bfloat16, device="cuda")
+    out = gdla.prefill_prefix(x["q_signal"], x["q_noise"], x["k"], x["v"], x["lam"], x["gate"],
+                              window=window, scale=scale, out=out)
+    torch.cuda.synchronize()
+    return out

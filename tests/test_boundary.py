@@ -132,3 +132,35 @@ def test_decode_rejections(lib):
 
 def test_decode_empty_is_noop(lib):
     assert decode(lib, [None] * 7, cu=None, B=0) == OK
+
+
+def prefill_prefix(lib, ptrs=None, B=1, Tq=64, P=100, n_kv=16, group=4, d_qk=192, d_v=128, window=0,
+                   scale=0.07):
+    if ptrs is None:
+        ptrs = [A + i * (1 << 32) for i in range(7)]
+    return lib.gdla_prefill_prefix(*ptrs, B, Tq, P, n_kv, group, d_qk, d_v, window,
+                                   ctypes.c_float(scale), None)
+
+
+def test_prefill_prefix_rejections(lib):
+    assert prefill_prefix(lib, P=-1) == INVALID
+    assert prefill_prefix(lib, Tq=-1) == INVALID
+    assert prefill_prefix(lib, group=2) == UNSUPPORTED
+    assert prefill_prefix(lib, window=-1) == INVALID
+    for i in range(7):
+        ptrs = [A + k * (1 << 32) for k in range(7)]
+        ptrs[i] = None
+        assert prefill_prefix(lib, ptrs) == INVALID
+    # the K span counts the prefix: P + T_q rows
+    assert prefill_prefix(lib, Tq=64, P=(1 << 21), n_kv=16) == UNSUPPORTED
+    assert b"2^31" in lib.gdla_last_error()
+    # out overlapping the prefix part of k (k spans B*(P+T_q) rows)
+    ptrs = [A + k * (1 << 32) for k in range(7)]
+    ptrs[6] = ptrs[2] + 64 * 16 * 192 * 2 + 4096        # inside k's prefix rows + new rows
+    assert prefill_prefix(lib, ptrs, Tq=64, P=100) == INVALID
+    assert b"overlaps k" in lib.gdla_last_error()
+
+
+def test_prefill_prefix_empty_is_noop(lib):
+    assert prefill_prefix(lib, [None] * 7, Tq=0) == OK
+    assert prefill_prefix(lib, [None] * 7, B=0) == OK

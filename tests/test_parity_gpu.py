@@ -16,8 +16,9 @@ import pytest
 import torch
 
 import workload as W
-from gdla_testutil import (compare, default_scale, gpu_decode, gpu_prefill, log, oracle_decode,
-                           oracle_prefill, oracle_prefill_rows, stratified_rows, to_dev)
+from gdla_testutil import (compare, default_scale, gpu_decode, gpu_prefill, gpu_prefill_prefix, log,
+                           oracle_decode, oracle_prefill, oracle_prefill_rows, query_tail,
+                           stratified_rows, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -239,3 +240,47 @@ def test_decode_configs_sampled(name):
                "cu_seqlens": torch.tensor([0, hi - lo], dtype=torch.int32),
                "lam": d["lam"][b:b + 1], "gate": d["gate"][b:b + 1]}
         compare(out[b:b + 1], oracle_decode(one, w.window), "%s seq %d L=%d" % (name, b, hi - lo))
+
+
+# ---------------------------------------------------------------------------
+# prefill after a prefix already in K/V (query row i at position P + i)
+# ---------------------------------------------------------------------------
+
+PREFIX_CASES = [
+    # (B, P, T_q, n_kv, window, dist): prefixes aligned and not aligned to the
+    # 64-key tiles, one and many query rows, full causal and windows
+    (1, 64, 64, 2, 0, "sharp"), (1, 100, 37, 2, 0, "sharp"), (2, 1, 200, 2, 0, "sharp"),
+    (1, 200, 1, 3, 0, "sharper"), (1, 333, 150, 2, 128, "sharp"), (1, 130, 260, 2, 1, "sharp"),
+    (1, 127, 129, 2, 129, "sharp"), (1, 300, 100, 2, 64, "cfg"), (1, 50, 300, 1, 1000, "sharp"),
+    (2, 191, 65, 4, 127, "sharper"),
+]
+
+
+@pytest.mark.parametrize("case", PREFIX_CASES, ids=lambda c: "B%d_P%d_Tq%d_kv%d_W%d_%s" % c)
+def test_prefill_prefix_matches_oracle_and_full_rows(case):
+    B, P, Tq, n_kv, window, dist = case
+    kw = {"cfg": {}, "sharp": SHARP, "sharper": SHARPER}[dist]
+    log("prefill prefix %s" % (case,))
+    x = to_dev(W.prefill_inputs(small(B, P + Tq, n_kv), seed=70 + P + Tq, **kw))
+    got = gpu_prefill_prefix(query_tail(x, P), window)
+    rb = np.repeat(np.arange(B, dtype=np.int32), Tq)
+    rt = np.tile(np.arange(P, P + Tq, dtype=np.int32), B)
+    want = oracle_prefill_rows(x, window, rb, rt).reshape(B, Tq, 4 * n_kv, 128)
+    compare(got, want, "prefix P=%d Tq=%d W=%d" % (P, Tq, window))
+    # the same query tiles and key tiles as the whole-sequence call: the same rows, bit for bit
+    assert torch.equal(got, gpu_prefill(x, window)[:, P:])
+
+
+def test_prefill_prefix_4k_after_28k_sampled():
+    """The chunked-prefill workload: the last 4096 tokens of a 32K sequence."""
+    P, Tq = 28672, 4096
+    w = W.Workload("prefix", "prefill", B=1, T=P + Tq, n_kv=16, window=0)
+    log("prefill prefix P=%d Tq=%d n_kv=16 sampled" % (P, Tq))
+    x = W.prefill_inputs(w, seed=71, device="cuda", **SHARP)
+    got = gpu_prefill_prefix(query_tail(x, P), 0)
+    rb, rt = stratified_rows(1, Tq, 16, 16, 24, seed=72)
+    want = oracle_prefill_rows(x, 0, rb, rt + P)
+    compare(got[0, torch.as_tensor(rt, dtype=torch.long, device=got.device)], want,
+            "prefix 4K after 28K sampled")
+    del x
+    torch.cuda.empty_cache()

@@ -42,6 +42,8 @@ class Workload:
     window: int = 0      # 0 = full causal, else keys t-W+1..t
     len_lo: int = 0      # decode: cached lengths ~ U{len_lo..len_hi}, new token included
     len_hi: int = 0
+    prefix: int = 0      # prefill after a prefix: the queries are positions prefix .. T-1
+                         # (inputs are drawn for all T positions; callers keep the query tail)
 
     @property
     def n_sig(self):
@@ -54,6 +56,11 @@ WORKLOADS = {
     "pf_full_4k": Workload("pf_full_4k", "prefill", B=1, T=4096),
     "pf_swa_32k": Workload("pf_swa_32k", "prefill", B=2, T=32768, window=WINDOW),
     "pf_full_128k": Workload("pf_full_128k", "prefill", B=1, T=131072),
+    # chunked prefill: the last 4096 tokens of a 32K sequence, full causal
+    "pf_prefix_4k_32k": Workload("pf_prefix_4k_32k", "prefill", B=1, T=32768, prefix=28672),
+    # one rank's share of the 32K sliding-window layer over 8 sequence-parallel
+    # GPUs: 4096 tokens after the 128 rows received from the left neighbour
+    "pf_swa_rank": Workload("pf_swa_rank", "prefill", B=2, T=4096 + WINDOW, window=WINDOW, prefix=WINDOW),
     "dec_full": Workload("dec_full", "decode", B=64, len_lo=8192, len_hi=65536),
     "dec_swa": Workload("dec_swa", "decode", B=64, len_lo=8192, len_hi=65536, window=WINDOW),
 }
