@@ -132,3 +132,50 @@ def decode(q_signal, q_noise, k_cache, v_cache, cu_seqlens, max_seqlen_k, lam, g
         out.data_ptr(), workspace.data_ptr(), workspace.numel(), B, n_kv, GROUP, D_QK, D_V,
         int(window), float(scale), _stream_ptr(k_cache.device)))
     return out
+
+
+D_C, D_R = 512, 64
+
+
+def decode_latent_workspace_size(B, n_kv, max_seqlen_k, window=0):
+    return int(_lib.load().gdla_decode_latent_workspace_size(B, n_kv, max_seqlen_k, int(window)))
+
+
+def decode_latent(q_signal, q_noise, latent_cache, cu_seqlens, max_seqlen_k, w_uk, w_uv, lam, gate,
+                  window=0, scale=None, out=None, workspace=None):
+    """Decode over a latent KV cache (compressed KV + shared rotary key per token).
+
+    q_signal [B,4*n_kv,192], q_noise [B,n_kv,192] (content 128, then rotary 64),
+    latent_cache [total,576], cu_seqlens int32 [B+1] (device), w_uk [n_kv,128,512],
+    w_uv [n_kv,128,512], lam [B,4*n_kv], gate [B,4*n_kv,128].  Returns out
+    [B,4*n_kv,128] bf16; equal to decode() over K_j = [w_uk[j] c ; k^R],
+    V_j = w_uv[j] c.  The workspace (uint8 device tensor) is allocated here if
+    not given.
+    """
+    total = latent_cache.shape[0]
+    n_kv = w_uk.shape[0]
+    B = q_signal.shape[0]
+    n_sig = n_kv * GROUP
+    _check(q_signal, "q_signal", (B, n_sig, D_QK))
+    _check(q_noise, "q_noise", (B, n_kv, D_QK))
+    _check(latent_cache, "latent_cache", (total, D_C + D_R))
+    _check(cu_seqlens, "cu_seqlens", (B + 1,), dtype=torch.int32)
+    _check(w_uk, "w_uk", (n_kv, D_QK - D_R, D_C))
+    _check(w_uv, "w_uv", (n_kv, D_V, D_C))
+    _check(lam, "lam", (B, n_sig))
+    _check(gate, "gate", (B, n_sig, D_V))
+    if out is None:
+        out = torch.empty((B, n_sig, D_V), dtype=torch.bfloat16, device=latent_cache.device)
+    _check(out, "out", (B, n_sig, D_V))
+    if scale is None:
+        scale = 1.0 / math.sqrt(D_QK)
+    need = decode_latent_workspace_size(B, n_kv, max_seqlen_k, window) if B > 0 else 0
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=latent_cache.device)
+    lib = _lib.load()
+    _lib.check(lib.gdla_decode_latent(
+        q_signal.data_ptr(), q_noise.data_ptr(), latent_cache.data_ptr(), cu_seqlens.data_ptr(),
+        int(max_seqlen_k), w_uk.data_ptr(), w_uv.data_ptr(), lam.data_ptr(), gate.data_ptr(),
+        out.data_ptr(), workspace.data_ptr(), workspace.numel(), B, n_kv, GROUP, D_C, D_R, D_V,
+        int(window), float(scale), _stream_ptr(latent_cache.device)))
+    return out

@@ -175,3 +175,69 @@ extern "C" int gdla_decode(const void *q_signal, const void *q_noise, const void
     if (e != hipSuccess) return fail(GDLA_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
     return GDLA_OK;
 }
+
+extern "C" size_t gdla_decode_latent_workspace_size(int B, int n_kv, int max_seqlen_k, int window) {
+    if (B < 1 || n_kv < 1 || max_seqlen_k < 1 || window < 0) return 0;
+    return gdla::latent_workspace_bytes(B, n_kv, gdla::latent_splits(max_seqlen_k, window));
+}
+
+extern "C" int gdla_decode_latent(const void *q_signal, const void *q_noise, const void *latent_cache,
+                                  const int32_t *cu_seqlens_k, int max_seqlen_k, const void *w_uk,
+                                  const void *w_uv, const void *lambda_, const void *gate, void *out,
+                                  void *workspace, size_t workspace_bytes, int B, int n_kv, int group,
+                                  int d_c, int d_r, int d_v, int window, float softmax_scale,
+                                  void *stream) {
+    g_last_error[0] = 0;
+    if (B < 0 || B > 65535) return fail(GDLA_ERR_INVALID_ARG, "B must be in [0, 65535] (got %d)", B);
+    if (n_kv < 1 || group < 1 || d_c < 1 || d_r < 0 || d_v < 1)
+        return fail(GDLA_ERR_INVALID_ARG, "n_kv, group, d_c, d_v must be >= 1 and d_r >= 0");
+    if (group != 4 || d_c != 512 || d_r != 64 || d_v != 128)
+        return fail(GDLA_ERR_UNSUPPORTED,
+                    "this build implements group=4, d_c=512, d_r=64, d_v=128 (got %d, %d, %d, %d)",
+                    group, d_c, d_r, d_v);
+    if (n_kv > 13107) return fail(GDLA_ERR_INVALID_ARG, "n_kv must be <= 13107 (got %d)", n_kv);
+    if (int rc = check_scale_window(softmax_scale, window)) return rc;
+    if (B == 0) return GDLA_OK;
+    if (max_seqlen_k < 1) return fail(GDLA_ERR_INVALID_ARG, "max_seqlen_k must be >= 1 (got %d)", max_seqlen_k);
+
+    const void *ptrs[8] = {q_signal, q_noise, latent_cache, w_uk, w_uv, lambda_, gate, out};
+    const char *names[8] = {"q_signal", "q_noise", "latent_cache", "w_uk", "w_uv", "lambda", "gate", "out"};
+    for (int i = 0; i < 8; ++i) {
+        if (!ptrs[i]) return fail(GDLA_ERR_INVALID_ARG, "%s is NULL", names[i]);
+        if (!aligned(ptrs[i], 16)) return fail(GDLA_ERR_MISALIGNED, "%s is not 16-byte aligned", names[i]);
+    }
+    if (!cu_seqlens_k) return fail(GDLA_ERR_INVALID_ARG, "cu_seqlens_k is NULL");
+    if (!aligned(cu_seqlens_k, 4)) return fail(GDLA_ERR_MISALIGNED, "cu_seqlens_k is not 4-byte aligned");
+    if ((long double)max_seqlen_k * (d_c + d_r) * 2 >= 4294967296.0L)
+        return fail(GDLA_ERR_UNSUPPORTED, "one sequence's latent rows must span < 2^32 bytes");
+
+    const int n_split = gdla::latent_splits(max_seqlen_k, window);
+    const size_t need = gdla::latent_workspace_bytes(B, n_kv, n_split);
+    if (!workspace) return fail(GDLA_ERR_WORKSPACE, "workspace is NULL, %zu bytes needed", need);
+    if (workspace_bytes < need)
+        return fail(GDLA_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
+    if (!aligned(workspace, 256)) return fail(GDLA_ERR_MISALIGNED, "workspace is not 256-byte aligned");
+
+    const uintptr_t ns = (uintptr_t)n_kv * group;
+    const Range o = {"out", (uintptr_t)out, (uintptr_t)out + (uintptr_t)B * ns * d_v * 2};
+    const Range w = {"workspace", (uintptr_t)workspace, (uintptr_t)workspace + need};
+    const int d_qk = d_v + d_r;                  // the content part of a query is d_v = 128 values
+    const Range in[6] = {
+        {"q_signal", (uintptr_t)q_signal, (uintptr_t)q_signal + (uintptr_t)B * ns * d_qk * 2},
+        {"q_noise", (uintptr_t)q_noise, (uintptr_t)q_noise + (uintptr_t)B * n_kv * d_qk * 2},
+        {"w_uk", (uintptr_t)w_uk, (uintptr_t)w_uk + (uintptr_t)n_kv * 128 * d_c * 2},
+        {"w_uv", (uintptr_t)w_uv, (uintptr_t)w_uv + (uintptr_t)n_kv * d_v * d_c * 2},
+        {"lambda", (uintptr_t)lambda_, (uintptr_t)lambda_ + (uintptr_t)B * ns * 2},
+        {"gate", (uintptr_t)gate, (uintptr_t)gate + (uintptr_t)B * ns * d_v * 2}};
+    for (const Range &x : in) {
+        if (overlaps(o, x)) return fail(GDLA_ERR_INVALID_ARG, "out overlaps %s", x.name);
+        if (overlaps(w, x)) return fail(GDLA_ERR_INVALID_ARG, "workspace overlaps %s", x.name);
+    }
+    if (overlaps(o, w)) return fail(GDLA_ERR_INVALID_ARG, "out overlaps workspace");
+
+    hipError_t e = gdla::launch_decode_latent(q_signal, q_noise, latent_cache, cu_seqlens_k, w_uk, w_uv,
+                                              lambda_, gate, out, workspace, B, n_kv, n_split, window,
+                                              softmax_scale, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(GDLA_ERR_HIP, "latent decode launch: %s", hipGetErrorString(e));
+    return GDLA_OK;
+}

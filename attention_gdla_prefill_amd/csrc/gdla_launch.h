@@ -26,4 +26,12 @@ hipError_t launch_decode(const void *qs, const void *qn, const void *kc, const v
                          void *workspace, int B, int n_kv, int n_split, int window, float scale,
                          hipStream_t stream);
 
+// Latent-cache decode: splits per sequence, workspace bytes, launch (3 kernels).
+int latent_splits(int max_seqlen_k, int window);
+size_t latent_workspace_bytes(int B, int n_kv, int n_split);
+hipError_t launch_decode_latent(const void *qs, const void *qn, const void *lat, const int32_t *cu,
+                                const void *wuk, const void *wuv, const void *lam, const void *gate,
+                                void *out, void *workspace, int B, int n_kv, int n_split, int window,
+                                float scale, hipStream_t stream);
+
 }  // namespace gdla

@@ -56,6 +56,13 @@ def decode_bytes(lengths, window, n_kv=16, n_sig=64):
     return sum(vis) * n_kv * (192 + 128) * 2 + len(lengths) * per_seq + 4 * (len(lengths) + 1)
 
 
+def decode_latent_bytes(lengths, window, n_kv=16, n_sig=64):
+    vis = [min(L, window) if window > 0 else L for L in lengths]
+    per_seq = 2 * (n_sig * 192 + n_kv * 192 + n_sig + 2 * n_sig * 128)
+    weights = 2 * n_kv * (128 + 128) * 512             # the two up-projections, read once
+    return sum(vis) * 576 * 2 + len(lengths) * per_seq + weights + 4 * (len(lengths) + 1)
+
+
 def source_hash():
     h = hashlib.sha256()
     for p in sorted(glob.glob(os.path.join(ROOT, "attention_gdla_prefill_amd", "csrc", "*"))):
@@ -222,6 +229,45 @@ def measured_peaks():
             "copy_1gib_gbs": copy_gbs, "copy_frac_of_peak": copy_gbs / PEAK_HBM_GBS}
 
 
+def bench_decode_latent(name, steps, warmup):
+    import torch
+    import attention_gdla_prefill_amd as gdla
+    import workload as W
+    w = W.WORKLOADS[name]
+    d = W.latent_decode_inputs(w, seed=0, device="cuda")
+    lengths = d["lengths"].tolist()
+    max_len = max(lengths)
+    out = torch.empty((w.B, w.n_sig, 128), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(gdla.decode_latent_workspace_size(w.B, w.n_kv, max_len, w.window),
+                     dtype=torch.uint8, device="cuda")
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    call = lambda: gdla.decode_latent(d["q_signal"], d["q_noise"], d["latent"], d["cu_seqlens"], max_len,
+                                      d["w_uk"], d["w_uv"], d["lam"], d["gate"], window=w.window,
+                                      out=out, workspace=ws)
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(steps):
+        flush.fill_(1)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        call()
+        b.record(stream)
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b))
+    kern_ms = sorted(times)[len(times) // 2]
+    nbytes = decode_latent_bytes(lengths, w.window)
+    expanded = decode_bytes(lengths, w.window)
+    del d, out, ws, flush
+    torch.cuda.empty_cache()
+    return {"kernel_ms": kern_ms, "bytes": nbytes, "gbs": nbytes / (kern_ms * 1e-3) / 1e9,
+            "hbm_frac": nbytes / (kern_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+            "expanded_equivalent_gbs": expanded / (kern_ms * 1e-3) / 1e9,
+            "cache": "cold (512 MB buffer rewritten before each launch)"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -234,7 +280,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--extras", default="pf_swa_32k,pf_full_128k,pf_prefix_4k_32k,pf_swa_rank,"
-                                        "dec_full,dec_swa",
+                                        "dec_full,dec_swa,dec_latent_full,dec_latent_swa",
                     help="comma-separated extra workloads to time (a profile of one workload "
                          "names just that one)")
     ap.add_argument("--copy-probe", action="store_true",
@@ -250,7 +296,7 @@ def main():
     wanted = [] if args.no_extra else [x for x in args.extras.split(",") if x]
     for name in wanted:
         if name not in ("pf_swa_32k", "pf_full_128k", "pf_prefix_4k_32k", "pf_swa_rank", "dec_full",
-                        "dec_swa"):
+                        "dec_swa", "dec_latent_full", "dec_latent_swa"):
             print("unknown extra workload %r" % name, file=sys.stderr)
             sys.exit(2)
 
@@ -285,11 +331,12 @@ def main():
             extra[name] = {"tflops": r["tflops"], "mfma_frac": r["tflops"] / PEAK_BF16_TFLOPS,
                            "gbs": r["gbs"], "hbm_frac": r["gbs"] / PEAK_HBM_GBS,
                            "kernel_ms": r["kernel_ms"], "steps": steps}
-        for name in ("dec_full", "dec_swa"):
+        for name in ("dec_full", "dec_swa", "dec_latent_full", "dec_latent_swa"):
             if name not in wanted:
                 continue
             print("[bench] extra %s" % name, file=sys.stderr, flush=True)
-            extra[name] = bench_decode(name, 10, 2)
+            fn = bench_decode_latent if name.startswith("dec_latent") else bench_decode
+            extra[name] = fn(name, 10, 2)
 
     peaks = measured_peaks() if args.peaks else None
 

@@ -165,6 +165,53 @@ int gdla_decode(const void *q_signal, const void *q_noise, const void *k_cache,
                 int B, int n_kv, int group, int d_qk, int d_v,
                 int window, float softmax_scale, void *stream);
 
+/*
+ * gdla_decode_latent_workspace_size -- bytes of device workspace
+ * gdla_decode_latent needs (never 0: it always holds the absorbed queries).
+ * Returns 0 for invalid arguments (gdla_decode_latent then rejects them).
+ */
+size_t gdla_decode_latent_workspace_size(int B, int n_kv, int max_seqlen_k, int window);
+
+/*
+ * gdla_decode_latent -- the decode of gdla_decode over a latent KV cache: the
+ * cache holds, per token, the normalised compressed KV c (d_c = 512 values)
+ * followed by the decoupled rotary key k^R (d_r = 64 values), shared by every
+ * KV head, instead of the expanded per-head K and V (aitrends.kr, GDLA and
+ * head-dimension paragraphs: the compressed KV of rank 512 is normalised once
+ * and expanded to the 16 KV heads; the rotary key is shared by all of them).
+ * KV head j's keys and values are
+ *     K_j[s] = [ W_uk[j] c_s ; k^R_s ]   (128 + 64 = 192 values)
+ *     V_j[s] =   W_uv[j] c_s             (128 values)
+ * and the result equals gdla_decode over those K and V.  The library does not
+ * form them: it folds W_uk into the queries and W_uv into the output, so each
+ * cache row (1,152 bytes) is read once for all query heads.
+ *
+ *   q_signal     [B, n_kv*group, 192]    content part (128) first, then rotary (64)
+ *   q_noise      [B, n_kv, 192]
+ *   latent_cache [total_k, d_c + d_r]    sequence b owns rows cu[b] .. cu[b+1]-1
+ *   cu_seqlens_k, max_seqlen_k           as for gdla_decode
+ *   w_uk         [n_kv, 128, d_c]        key up-projection: k^C = w_uk[j] c
+ *   w_uv         [n_kv, d_v, d_c]        value up-projection: v = w_uv[j] c
+ *   lambda_      [B, n_kv*group]
+ *   gate         [B, n_kv*group, d_v]
+ *   out          [B, n_kv*group, d_v]    every element written; no overlap with inputs
+ *   workspace    device scratch of at least
+ *                gdla_decode_latent_workspace_size(B, n_kv, max_seqlen_k, window)
+ *                bytes, 256-byte aligned; contents on entry are ignored;
+ *                calls sharing one workspace must be ordered on one stream
+ *
+ * The absorbed queries are rounded to bf16 before the scores (the only
+ * rounding the expanded path does not have).  B = 0 is a valid empty call.
+ * This build supports group = 4, d_c = 512, d_r = 64, d_v = 128; other
+ * shapes return GDLA_ERR_UNSUPPORTED.
+ */
+int gdla_decode_latent(const void *q_signal, const void *q_noise, const void *latent_cache,
+                       const int32_t *cu_seqlens_k, int max_seqlen_k, const void *w_uk,
+                       const void *w_uv, const void *lambda_, const void *gate, void *out,
+                       void *workspace, size_t workspace_bytes,
+                       int B, int n_kv, int group, int d_c, int d_r, int d_v,
+                       int window, float softmax_scale, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -10,7 +10,9 @@ two-pass softmax).  This module only marshals numpy arrays into it:
 * :func:`prefill` -- every query position of a [B, T] prefill;
 * :func:`prefill_rows` -- a chosen list of (b, t) positions, for workloads too
   large to check in full (the oracle is per row, so sampling is exact);
-* :func:`decode` -- one new query per sequence over a packed KV cache.
+* :func:`decode` -- one new query per sequence over a packed KV cache;
+* :func:`decode_latent` -- the same over a latent (compressed) KV cache, with
+  the per-head keys and values formed by explicit up-projection.
 
 Inputs are float32 arrays (bf16 tensors widen to float32 exactly); outputs are
 float64 arrays, never rounded.
@@ -40,6 +42,11 @@ def _bind(path):
     lib.gdla_oracle_decode.argtypes = [
         _f32p, _f32p, _f32p, _f32p, _i32p, _f32p, _f32p, ctypes.c_int, ctypes.c_int,
         ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_double, _f64p]
+    lib.gdla_oracle_decode_latent.restype = ctypes.c_int
+    lib.gdla_oracle_decode_latent.argtypes = [
+        _f32p, _f32p, _f32p, _f32p, _f32p, _i32p, _f32p, _f32p, ctypes.c_int, ctypes.c_int,
+        ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+        ctypes.c_double, _f64p]
     lib.gdla_oracle_num_threads.restype = ctypes.c_int
     lib.gdla_oracle_num_threads.argtypes = []
     return lib
@@ -129,4 +136,35 @@ def decode(q_signal, q_noise, k_cache, v_cache, cu_seqlens, lam, gate, window=0,
                               group, d_qk, d_v, int(window), float(scale), out)
     if rc != 0:
         raise ValueError("oracle decode rejected its arguments (code %d)" % rc)
+    return out
+
+
+def decode_latent(q_signal, q_noise, latent, w_uk, w_uv, cu_seqlens, lam, gate, window=0,
+                  scale=None, lib=None):
+    """Decode over a latent cache.
+
+    latent [total, d_c + d_r] (compressed KV, then the shared rotary key),
+    w_uk [n_kv, d_kc, d_c], w_uv [n_kv, d_v, d_c], q_signal [B, n_kv*g, d_kc + d_r],
+    q_noise [B, n_kv, d_kc + d_r] -> float64 [B, n_kv*g, d_v].
+    """
+    qs = _f32(q_signal)
+    B, n_sig, d_qk = qs.shape
+    wk = _f32(w_uk)
+    wv = _f32(w_uv)
+    n_kv, d_kc, d_c = wk.shape
+    d_v = wv.shape[1]
+    d_r = d_qk - d_kc
+    lat = _f32(latent)
+    assert lat.shape[1] == d_c + d_r, lat.shape
+    group = n_sig // n_kv
+    if scale is None:
+        scale = 1.0 / np.sqrt(d_qk)
+    out = np.empty((B, n_sig, d_v), dtype=np.float64)
+    cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int32))
+    L = lib if lib is not None else library()
+    rc = L.gdla_oracle_decode_latent(qs, _f32(q_noise), lat, wk, wv, cu, _f32(lam), _f32(gate), B,
+                                     n_kv, group, d_c, d_r, d_kc, d_v, int(window), float(scale),
+                                     out)
+    if rc != 0:
+        raise ValueError("oracle latent decode rejected its arguments (code %d)" % rc)
     return out

@@ -296,6 +296,136 @@ int gdla_oracle_decode(const float *q_signal, const float *q_noise, const float 
     return failed ? ORACLE_NO_MEMORY : ORACLE_OK;
 }
 
+/*
+ * Decode over a latent (compressed) KV cache.  Each cache row holds the
+ * normalised compressed KV c (d_c values) followed by the decoupled rotary key
+ * k^R (d_r values), shared by every KV head.  KV head j's key and value rows
+ * are the up-projections (aitrends.kr, GDLA paragraph: the compressed KV is
+ * normalised once, expanded to the 16 KV heads, and the rotary key is shared
+ * by all of them):
+ *   K_j[s] = [ W_uk[j] c_s ; k^R_s ]   (d_qk = d_kc + d_r values)
+ *   V_j[s] =   W_uv[j] c_s             (d_v values)
+ * with W_uk [n_kv][d_kc][d_c], W_uv [n_kv][d_v][d_c].  Everything else is the
+ * decode definition above.  Here the keys and values are formed explicitly, in
+ * fp64, for the visible rows of each sequence, and the softmax runs over them.
+ *   latent  [total][d_c + d_r]
+ *   q_signal [B][n_kv*group][d_kc + d_r]   (content part first, then rotary)
+ */
+int gdla_oracle_decode_latent(const float *q_signal, const float *q_noise, const float *latent,
+                              const float *w_uk, const float *w_uv, const int32_t *cu_seqlens,
+                              const float *lam, const float *gate, int B, int n_kv, int group,
+                              int d_c, int d_r, int d_kc, int d_v, int window, double scale,
+                              double *out)
+{
+    if (B < 0 || window < 0 || d_c < 1 || d_r < 0 || d_kc < 1 || !dims_ok(n_kv, group, d_kc + d_r, d_v))
+        return ORACLE_BAD_ARG;
+    if (B == 0)
+        return ORACLE_OK;
+    if (!q_signal || !q_noise || !latent || !w_uk || !w_uv || !cu_seqlens || !lam || !gate || !out)
+        return ORACLE_BAD_ARG;
+    long max_len = 0;
+    for (int b = 0; b < B; ++b) {
+        long len = (long)cu_seqlens[b + 1] - cu_seqlens[b];
+        if (cu_seqlens[b] < 0 || len < 1)
+            return ORACLE_BAD_ARG;
+        if (len > max_len)
+            max_len = len;
+    }
+    const int d_qk = d_kc + d_r, n_sig = n_kv * group, row = d_c + d_r;
+    int failed = 0;
+
+#pragma omp parallel
+    {
+        double *kx = (double *)malloc(sizeof(double) * (size_t)max_len * (size_t)d_qk);
+        double *vx = (double *)malloc(sizeof(double) * (size_t)max_len * (size_t)d_v);
+        double *z = (double *)malloc(sizeof(double) * (size_t)max_len);
+        double *hn = (double *)malloc(sizeof(double) * (size_t)d_v);
+        double *hs = (double *)malloc(sizeof(double) * (size_t)d_v);
+        if (!kx || !vx || !z || !hn || !hs) {
+#pragma omp atomic write
+            failed = 1;
+        } else {
+#pragma omp for schedule(dynamic, 1)
+            for (long w = 0; w < (long)B * n_kv; ++w) {
+                const long b = w / n_kv;
+                const int j = (int)(w % n_kv);
+                const long len = (long)cu_seqlens[b + 1] - cu_seqlens[b];
+                const long s_lo = first_visible(len - 1, window), n = len - s_lo;
+                /* the visible keys and values of KV head j, expanded */
+                for (long i = 0; i < n; ++i) {
+                    const float *lr = latent + ((long)cu_seqlens[b] + s_lo + i) * row;
+                    for (int d = 0; d < d_kc; ++d) {
+                        double acc = 0.0;
+                        for (int c = 0; c < d_c; ++c)
+#if ORACLE_MUTANT == 9
+                            /* planted: W_uk read as [d_c][d_kc] */
+                            acc += (double)w_uk[(long)j * d_kc * d_c + (long)c * d_kc + d] * (double)lr[c];
+#else
+                            acc += (double)w_uk[((long)j * d_kc + d) * d_c + c] * (double)lr[c];
+#endif
+                        kx[i * d_qk + d] = acc;
+                    }
+                    for (int d = 0; d < d_r; ++d)
+#if ORACLE_MUTANT == 8
+                        kx[i * d_qk + d_kc + d] = 0.0;           /* planted: rotary key dropped */
+#else
+                        kx[i * d_qk + d_kc + d] = (double)lr[d_c + d];
+#endif
+                    for (int d = 0; d < d_v; ++d) {
+#if ORACLE_MUTANT == 10
+                        const float *wr = w_uk + ((long)j * d_v + d) * d_c;   /* planted: V from W_uk */
+#else
+                        const float *wr = w_uv + ((long)j * d_v + d) * d_c;
+#endif
+                        double acc = 0.0;
+                        for (int c = 0; c < d_c; ++c)
+                            acc += (double)wr[c] * (double)lr[c];
+                        vx[i * d_v + d] = acc;
+                    }
+                }
+                /* noise head j, then the group's signal heads (interleave) */
+                for (int hh = -1; hh < group; ++hh) {
+                    const float *q = hh < 0 ? q_noise + (b * n_kv + j) * (long)d_qk
+                                            : q_signal + (b * n_sig + (long)j * group + hh) * d_qk;
+                    double *h = hh < 0 ? hn : hs;
+                    double zmax = -INFINITY;
+                    for (long i = 0; i < n; ++i) {
+                        double dot = 0.0;
+                        for (int d = 0; d < d_qk; ++d)
+                            dot += (double)q[d] * kx[i * d_qk + d];
+                        z[i] = scale * dot;
+                        if (z[i] > zmax)
+                            zmax = z[i];
+                    }
+                    double denom = 0.0;
+                    for (int c = 0; c < d_v; ++c)
+                        h[c] = 0.0;
+                    for (long i = 0; i < n; ++i) {
+                        const double e = exp(z[i] - zmax);
+                        denom += e;
+                        for (int c = 0; c < d_v; ++c)
+                            h[c] += e * vx[i * d_v + c];
+                    }
+                    for (int c = 0; c < d_v; ++c)
+                        h[c] /= denom;
+                    if (hh < 0)
+                        continue;
+                    const long o = (b * n_sig + (long)j * group + hh) * d_v;
+                    const double l = (double)lam[b * n_sig + (long)j * group + hh];
+                    for (int c = 0; c < d_v; ++c)
+                        out[o + c] = (double)gate[o + c] * (hs[c] - l * hn[c]);
+                }
+            }
+        }
+        free(kx);
+        free(vx);
+        free(z);
+        free(hn);
+        free(hs);
+    }
+    return failed ? ORACLE_NO_MEMORY : ORACLE_OK;
+}
+
 /* Number of OpenMP threads a parallel region of this library would use. */
 int gdla_oracle_num_threads(void)
 {

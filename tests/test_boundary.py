@@ -164,3 +164,40 @@ def test_prefill_prefix_rejections(lib):
 def test_prefill_prefix_empty_is_noop(lib):
     assert prefill_prefix(lib, [None] * 7, Tq=0) == OK
     assert prefill_prefix(lib, [None] * 7, B=0) == OK
+
+
+def decode_latent(lib, ptrs=None, cu=A + 0x700000000, max_len=4096, ws=A + 0x900000000, ws_bytes=1 << 40,
+                  B=2, n_kv=16, group=4, d_c=512, d_r=64, d_v=128, window=0, scale=0.07):
+    if ptrs is None:
+        ptrs = [A + i * (1 << 32) for i in range(8)]
+    qs, qn, lat, wuk, wuv, lam, gate, out = ptrs
+    return lib.gdla_decode_latent(qs, qn, lat, cu, max_len, wuk, wuv, lam, gate, out, ws, ws_bytes, B,
+                                  n_kv, group, d_c, d_r, d_v, window, ctypes.c_float(scale), None)
+
+
+def test_decode_latent_workspace_size(lib):
+    one = lib.gdla_decode_latent_workspace_size(64, 16, 128, 128)
+    assert one > 0
+    assert lib.gdla_decode_latent_workspace_size(64, 16, 65536, 0) > one
+    assert lib.gdla_decode_latent_workspace_size(0, 16, 100, 0) == 0
+
+
+def test_decode_latent_rejections(lib):
+    assert decode_latent(lib, B=-1) == INVALID
+    assert decode_latent(lib, group=2) == UNSUPPORTED
+    assert decode_latent(lib, d_c=256) == UNSUPPORTED
+    assert decode_latent(lib, d_r=32) == UNSUPPORTED
+    assert decode_latent(lib, window=-1) == INVALID
+    assert decode_latent(lib, max_len=0) == INVALID
+    assert decode_latent(lib, cu=None) == INVALID
+    for i in range(8):
+        ptrs = [A + k * (1 << 32) for k in range(8)]
+        ptrs[i] = None
+        assert decode_latent(lib, ptrs) == INVALID
+        ptrs[i] = A + 8 + i * (1 << 32)
+        assert decode_latent(lib, ptrs) == MISALIGNED
+    need = lib.gdla_decode_latent_workspace_size(2, 16, 4096, 0)
+    assert decode_latent(lib, ws=None) == WORKSPACE
+    assert decode_latent(lib, ws_bytes=need - 1) == WORKSPACE
+    assert decode_latent(lib, ws=A + 0x900000000 + 128, ws_bytes=need) == MISALIGNED
+    assert decode_latent(lib, [None] * 8, cu=None, B=0) == OK

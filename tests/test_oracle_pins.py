@@ -368,7 +368,77 @@ def test_oracle_rejects_bad_arguments():
 
 
 # ----------------------------------------------------------------------------
-# 10. every planted mistake fails at least one pin
+# 10. latent-cache decode: the same result as the expanded cache it stands for
+# ----------------------------------------------------------------------------
+
+def latent_inputs(lengths, n_kv, seed, d_c=512, d_r=64, d_kc=128, d_v=128):
+    r = np.random.default_rng(seed)
+    B, n_sig = len(lengths), 4 * n_kv
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    total = int(cu[-1])
+    f = lambda *shape, s=1.0: (r.standard_normal(shape) * s).astype(np.float32)
+    return dict(q_signal=f(B, n_sig, d_kc + d_r, s=0.3), q_noise=f(B, n_kv, d_kc + d_r, s=0.3),
+                latent=f(total, d_c + d_r), w_uk=f(n_kv, d_kc, d_c, s=0.05),
+                w_uv=f(n_kv, d_v, d_c, s=0.05), cu_seqlens=cu,
+                lam=r.uniform(0, 1, (B, n_sig)).astype(np.float32),
+                gate=r.uniform(0, 1, (B, n_sig, d_v)).astype(np.float32))
+
+
+def expand_latent(x, d_c=512):
+    """Per-head K and V by explicit up-projection (numpy, float64)."""
+    c = x["latent"][:, :d_c].astype(np.float64)
+    kr = x["latent"][:, d_c:].astype(np.float64)
+    kc = np.einsum("jdc,sc->sjd", x["w_uk"].astype(np.float64), c)
+    k = np.concatenate([kc, np.broadcast_to(kr[:, None, :], (c.shape[0], kc.shape[1], kr.shape[1]))],
+                       axis=2)
+    v = np.einsum("jdc,sc->sjd", x["w_uv"].astype(np.float64), c)
+    return k, v
+
+
+def latent_oracle(x, window, lib=None):
+    return oracle.decode_latent(x["q_signal"], x["q_noise"], x["latent"], x["w_uk"], x["w_uv"],
+                                x["cu_seqlens"], x["lam"], x["gate"], window=window, lib=lib)
+
+
+def check_latent_equals_expanded(lib=None, windows=(0, 1, 5)):
+    x = latent_inputs([1, 7, 23], 2, seed=40)
+    k, v = expand_latent(x)
+    for window in windows:
+        got = latent_oracle(x, window, lib)
+        # the expanded path is pinned above; K and V widen from float64 to its float32 inputs
+        want = oracle.decode(x["q_signal"], x["q_noise"], k.astype(np.float32), v.astype(np.float32),
+                             x["cu_seqlens"], x["lam"], x["gate"], window=window)
+        np.testing.assert_allclose(got, want, rtol=1e-5, atol=1e-6)
+
+
+def test_latent_decode_equals_expanded_decode():
+    check_latent_equals_expanded()
+
+
+def check_latent_window_one(lib=None):
+    # W = 1: each sequence's query sees only its last row, so out = gate (1 - lambda) W_uv[j] c_last
+    x = latent_inputs([3, 1, 12], 3, seed=41)
+    got = latent_oracle(x, 1, lib)
+    last = x["latent"][x["cu_seqlens"][1:] - 1, :512].astype(np.float64)        # [B, 512]
+    vj = np.einsum("jdc,bc->bjd", x["w_uv"].astype(np.float64), last)           # [B, n_kv, 128]
+    want = (x["gate"].astype(np.float64) * (1.0 - x["lam"].astype(np.float64))[:, :, None]
+            * np.repeat(vj, 4, axis=1))
+    np.testing.assert_allclose(got, want, rtol=1e-9, atol=1e-12)
+
+
+def test_latent_window_one_is_last_value():
+    check_latent_window_one()
+
+
+def test_latent_lambda1_identical_queries_give_zero():
+    x = latent_inputs([5, 30], 2, seed=42)
+    x["q_signal"] = np.repeat(x["q_noise"], 4, axis=1)
+    x["lam"] = np.ones_like(x["lam"])
+    assert np.array_equal(latent_oracle(x, 0), np.zeros_like(x["gate"], dtype=np.float64))
+
+
+# ----------------------------------------------------------------------------
+# 11. every planted mistake fails at least one pin
 # ----------------------------------------------------------------------------
 
 MUTANTS = {
@@ -379,6 +449,9 @@ MUTANTS = {
     5: "rotary tail of the query-key dot product dropped",
     6: "softmax scale forgotten",
     7: "V read from the wrong KV head",
+    8: "latent decode: rotary key dropped",
+    9: "latent decode: W_uk read transposed",
+    10: "latent decode: values up-projected with W_uk",
 }
 
 
@@ -391,6 +464,8 @@ def pin_suite(lib):
         "constant_v": lambda: check_constant_v(lib),
         "zero_q_mean": lambda: check_zero_q_prefix_mean(lib, windows=(0, 5)),
         "affine_lambda": lambda: check_affine_lambda(lib),
+        "latent_expanded": lambda: check_latent_equals_expanded(lib, windows=(0, 5)),
+        "latent_window_one": lambda: check_latent_window_one(lib),
     }
     failed = []
     for name, fn in checks.items():

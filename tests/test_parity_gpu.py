@@ -284,3 +284,76 @@ def test_prefill_prefix_4k_after_28k_sampled():
             "prefix 4K after 28K sampled")
     del x
     torch.cuda.empty_cache()
+
+
+# ---------------------------------------------------------------------------
+# decode over the latent cache (compressed KV 512 + shared rotary key 64)
+# ---------------------------------------------------------------------------
+
+def latent_workload(n_kv, lengths, window=0):
+    w = W.Workload("latent", "decode_latent", B=len(lengths), n_kv=n_kv, window=window)
+    return w, lengths
+
+
+def gpu_decode_latent(d, max_len, window):
+    import attention_gdla_prefill_amd as gdla
+    B, n_sig = d["q_signal"].shape[:2]
+    out = torch.full((B, n_sig, 128), float("nan"), dtype=torch.bfloat16, device="cuda")
+    out = gdla.decode_latent(d["q_signal"], d["q_noise"], d["latent"], d["cu_seqlens"], max_len,
+                             d["w_uk"], d["w_uv"], d["lam"], d["gate"], window=window, out=out)
+    torch.cuda.synchronize()
+    return out
+
+
+def oracle_decode_latent(d, window):
+    import oracle
+    f = lambda t: t.detach().float().cpu().numpy()
+    return oracle.decode_latent(f(d["q_signal"]), f(d["q_noise"]), f(d["latent"]), f(d["w_uk"]),
+                                f(d["w_uv"]), d["cu_seqlens"].cpu().numpy().astype(np.int32),
+                                f(d["lam"]), f(d["gate"]), window=window)
+
+
+LATENT_CASES = [
+    # (n_kv, lengths, window, q_std): 80 heads = one full head group; 10 and 85 heads
+    (16, [1, 2, 31, 32, 33, 100], 0, None), (16, [1, 2, 31, 32, 33, 100], 1, None),
+    (16, [5, 200, 129], 128, 1.0), (2, [7, 64, 300], 0, 1.0), (17, [40, 3], 0, 1.0),
+    (2, [9000, 4097, 12], 0, 1.0), (2, [9000, 130], 128, 1.0),
+]
+
+
+@pytest.mark.parametrize("case", LATENT_CASES, ids=lambda c: "kv%d_L%s_W%d" % (c[0], "-".join(map(str, c[1])), c[2]))
+def test_decode_latent_matches_oracle(case):
+    n_kv, lengths, window, q_std = case
+    log("latent decode n_kv=%d lengths=%s W=%d" % (n_kv, lengths, window))
+    w, _ = latent_workload(n_kv, lengths, window)
+    d = to_dev(W.latent_decode_inputs(w, seed=80 + len(lengths) + n_kv, lengths=torch.tensor(lengths),
+                                      q_std=q_std))
+    compare(gpu_decode_latent(d, max(lengths), window), oracle_decode_latent(d, window),
+            "latent decode kv%d W%d" % (n_kv, window))
+
+
+@pytest.mark.parametrize("name", ["dec_latent_full", "dec_latent_swa"])
+def test_decode_latent_configs_sampled(name):
+    """The 64-sequence configs; sampled sequences checked against the expanded
+    decode definition (K and V formed from the latent rows by a float64 matmul)."""
+    import oracle
+    w = W.WORKLOADS[name]
+    log("latent decode config %s" % name)
+    d = W.latent_decode_inputs(w, seed=0, device="cuda")
+    lengths = d["lengths"].tolist()
+    got = gpu_decode_latent(d, max(lengths), w.window)
+    cu = d["cu_seqlens"].cpu().numpy()
+    order = np.argsort(lengths)
+    for b in [int(order[0]), int(order[len(order) // 2])]:
+        lo = int(cu[b] if w.window == 0 else max(cu[b], cu[b + 1] - w.window))
+        lat = d["latent"][lo:int(cu[b + 1])].double()
+        k = torch.cat([torch.einsum("jdc,sc->sjd", d["w_uk"].double(), lat[:, :512]),
+                       lat[:, None, 512:].expand(-1, w.n_kv, -1)], dim=2)
+        v = torch.einsum("jdc,sc->sjd", d["w_uv"].double(), lat[:, :512])
+        f = lambda t: t.detach().float().cpu().numpy()
+        want = oracle.decode(f(d["q_signal"][b:b + 1]), f(d["q_noise"][b:b + 1]), f(k), f(v),
+                             np.array([0, k.shape[0]], np.int32), f(d["lam"][b:b + 1]),
+                             f(d["gate"][b:b + 1]), window=0)
+        compare(got[b:b + 1], want, "%s seq %d (L=%d)" % (name, b, lengths[b]))
+    del d
+    torch.cuda.empty_cache()

@@ -63,6 +63,10 @@ WORKLOADS = {
     "pf_swa_rank": Workload("pf_swa_rank", "prefill", B=2, T=4096 + WINDOW, window=WINDOW, prefix=WINDOW),
     "dec_full": Workload("dec_full", "decode", B=64, len_lo=8192, len_hi=65536),
     "dec_swa": Workload("dec_swa", "decode", B=64, len_lo=8192, len_hi=65536, window=WINDOW),
+    # the same decodes over the latent cache (compressed KV 512 + rotary key 64)
+    "dec_latent_full": Workload("dec_latent_full", "decode_latent", B=64, len_lo=8192, len_hi=65536),
+    "dec_latent_swa": Workload("dec_latent_swa", "decode_latent", B=64, len_lo=8192, len_hi=65536,
+                               window=WINDOW),
 }
 
 
@@ -135,3 +139,45 @@ def decode_inputs(w, seed=0, device="cpu", lengths=None, q_std=None, k_std=None,
     out["gate"] = _bf16(torch.sigmoid(_draw(gen, (B, w.n_sig, w.d_v), device, 1.0)))
     return out
 
+
+D_C = 512            # compressed KV rank (aitrends.kr, head-dimension paragraph)
+D_R = 64             # rotary key dims, shared by every KV head
+
+
+def latent_decode_inputs(w, seed=0, device="cpu", lengths=None, q_std=None):
+    """bf16 tensors for a decode over the latent cache.
+
+    Returns dict with q_signal [B,n_sig,192], q_noise [B,n_kv,192] (content
+    128, then rotary 64), latent [total, 512+64] (compressed KV, then the
+    shared rotary key), w_uk [n_kv,128,512], w_uv [n_kv,128,512],
+    cu_seqlens int32 [B+1] (on ``device``), lengths int64 [B] (CPU),
+    lam [B,n_sig], gate [B,n_sig,128].  The compressed KV is the output of a
+    normalisation, N(0,1) per value; the up-projections are N(0,1)/sqrt(192*512),
+    so the expanded keys and values have the N(0,1)/sqrt(192) spread of the
+    expanded-cache workloads.  Draw order: q_signal, q_noise, latent, w_uk,
+    w_uv, lambda, gate.
+    """
+    if lengths is None:
+        lengths = decode_lengths(w, seed)
+    lengths = torch.as_tensor(lengths, dtype=torch.int64).cpu()
+    base = 1.0 / math.sqrt(w.d_qk)
+    q_std = base if q_std is None else q_std
+    cu = torch.zeros(lengths.numel() + 1, dtype=torch.int64)
+    cu[1:] = torch.cumsum(lengths, 0)
+    total = int(cu[-1])
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    B = lengths.numel()
+    d_kc = w.d_qk - D_R
+    out = {"lengths": lengths, "cu_seqlens": cu.to(torch.int32).to(device)}
+    out["q_signal"] = _bf16(_draw(gen, (B, w.n_sig, w.d_qk), device, q_std))
+    out["q_noise"] = _bf16(_draw(gen, (B, w.n_kv, w.d_qk), device, q_std))
+    lat = _draw(gen, (total, D_C + D_R), device, 1.0)
+    lat[:, D_C:] *= base
+    out["latent"] = _bf16(lat)
+    wstd = 1.0 / math.sqrt(w.d_qk * D_C)
+    out["w_uk"] = _bf16(_draw(gen, (w.n_kv, d_kc, D_C), device, wstd))
+    out["w_uv"] = _bf16(_draw(gen, (w.n_kv, w.d_v, D_C), device, wstd))
+    out["lam"] = _bf16(torch.rand((B, w.n_sig), generator=gen, device=device))
+    out["gate"] = _bf16(torch.sigmoid(_draw(gen, (B, w.n_sig, w.d_v), device, 1.0)))
+    return out
