@@ -332,6 +332,30 @@ def test_decode_latent_matches_oracle(case):
             "latent decode kv%d W%d" % (n_kv, window))
 
 
+def test_decode_latent_score_spikes():
+    """Keys whose scores stand far above the rest of their chunk.
+
+    The rotary key part of a few cache rows is scaled by 3000, which moves
+    their scores by about +-180 in log2 units for every head (the values,
+    W_uv c, are untouched).  A spike in a chunk's first tile fixes a high
+    reference (the later keys of the chunk vanish against it); a spike later in
+    a chunk exceeds the first tile's reference by far more than the weight
+    sums can hold, so the chunk is redone against its exact maxima.  Both must
+    give the softmax of the oracle."""
+    n_kv, lengths = 2, [300, 5000, 70]
+    log("latent decode score spikes lengths=%s" % lengths)
+    w, _ = latent_workload(n_kv, lengths)
+    d = W.latent_decode_inputs(w, seed=91, lengths=torch.tensor(lengths), q_std=1.0)
+    cu = d["cu_seqlens"].tolist()
+    # (sequence, key): chunks of 150 / 2500 / 35 keys (two splits at this maximum length)
+    for b, key in [(0, 0), (0, 200), (1, 1000), (1, 4000), (2, 40 - 6)]:
+        row = d["latent"][cu[b] + key].float()
+        row[512:] *= 3000.0
+        d["latent"][cu[b] + key] = row.to(torch.bfloat16)
+    d = to_dev(d)
+    compare(gpu_decode_latent(d, max(lengths), 0), oracle_decode_latent(d, 0), "latent decode score spikes")
+
+
 @pytest.mark.parametrize("name", ["dec_latent_full", "dec_latent_swa"])
 def test_decode_latent_configs_sampled(name):
     """The 64-sequence configs; sampled sequences checked against the expanded
