@@ -12,7 +12,9 @@ two-pass softmax).  This module only marshals numpy arrays into it:
   large to check in full (the oracle is per row, so sampling is exact);
 * :func:`decode` -- one new query per sequence over a packed KV cache;
 * :func:`decode_latent` -- the same over a latent (compressed) KV cache, with
-  the per-head keys and values formed by explicit up-projection.
+  the per-head keys and values formed by explicit up-projection;
+* :func:`prep` -- the step ahead of the attention core: rotary embedding of
+  the query heads and of the shared rotary key, lambda and the gate.
 
 Inputs are float32 arrays (bf16 tensors widen to float32 exactly); outputs are
 float64 arrays, never rounded.
@@ -47,6 +49,11 @@ def _bind(path):
         _f32p, _f32p, _f32p, _f32p, _f32p, _i32p, _f32p, _f32p, ctypes.c_int, ctypes.c_int,
         ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
         ctypes.c_double, _f64p]
+    lib.gdla_oracle_prep.restype = ctypes.c_int
+    lib.gdla_oracle_prep.argtypes = [
+        _f32p, _f32p, _f32p, _f32p, _f32p, _f32p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+        ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_double,
+        _f64p, _f64p, _f64p, _f64p, _f64p]
     lib.gdla_oracle_num_threads.restype = ctypes.c_int
     lib.gdla_oracle_num_threads.argtypes = []
     return lib
@@ -167,4 +174,32 @@ def decode_latent(q_signal, q_noise, latent, w_uk, w_uv, cu_seqlens, lam, gate, 
                                      out)
     if rc != 0:
         raise ValueError("oracle latent decode rejected its arguments (code %d)" % rc)
+    return out
+
+
+def prep(q_signal, q_noise, k_rope, x, w_lambda, gate_pre, pos0=0, theta=10000.0, lib=None):
+    """The step ahead of the attention core.
+
+    q_signal [B, T, n_sig, d_qk], q_noise [B, T, n_kv, d_qk], k_rope [B, T, 64],
+    x [B, T, d_model], w_lambda [n_sig, d_model], gate_pre [B, T, n_sig, d_v]
+    -> dict of float64 arrays: q_signal, q_noise (rotary parts rotated), k_rot
+    [B, T, n_kv, 64] (the rotated shared key as it lands in each KV head), lam
+    [B, T, n_sig] and gate [B, T, n_sig, d_v].
+    """
+    qs, qn, kr = _f32(q_signal), _f32(q_noise), _f32(k_rope)
+    xx, wl, gp = _f32(x), _f32(w_lambda), _f32(gate_pre)
+    B, T, n_sig, d_qk = qs.shape
+    n_kv = qn.shape[2]
+    d_model = xx.shape[2]
+    d_v = gp.shape[3]
+    assert kr.shape == (B, T, 64) and wl.shape == (n_sig, d_model), (kr.shape, wl.shape)
+    out = {"q_signal": np.empty(qs.shape, np.float64), "q_noise": np.empty(qn.shape, np.float64),
+           "k_rot": np.empty((B, T, n_kv, 64), np.float64), "lam": np.empty((B, T, n_sig), np.float64),
+           "gate": np.empty(gp.shape, np.float64)}
+    L = lib if lib is not None else library()
+    rc = L.gdla_oracle_prep(qs, qn, kr, xx, wl, gp, B, T, n_kv, n_sig // n_kv, d_qk, d_v, d_model,
+                            int(pos0), float(theta), out["q_signal"], out["q_noise"], out["k_rot"],
+                            out["lam"], out["gate"])
+    if rc != 0:
+        raise ValueError("oracle prep rejected its arguments (code %d)" % rc)
     return out

@@ -426,6 +426,122 @@ int gdla_oracle_decode_latent(const float *q_signal, const float *q_noise, const
     return failed ? ORACLE_NO_MEMORY : ORACLE_OK;
 }
 
+/*
+ * ---- The step ahead of the attention core (rotary embedding, lambda, gate).
+ *
+ * Sources: aitrends.kr (page above), GDLA paragraph: the query path expands
+ * the compressed query into a content query and a rotary query; the KV path
+ * produces a decoupled rotary key next to the compressed KV; lambda_t =
+ * sigmoid(x_t W^lambda) from the input hidden state; a query-based
+ * element-wise gate follows the subtraction.  Head-dimension paragraph: the
+ * rotary component is 64 values of the 192, and the rotary key is shared by
+ * every KV head.  metalmedia (page 2), Table 1: hidden dimension 4,096 and
+ * output gating.
+ *
+ * Readings where the pages are silent (listed in the design notes):
+ *   - the rotary part is the last 64 of a head's 192 values (content first);
+ *   - the rotation is the original rotary position embedding: adjacent pairs
+ *     (2i, 2i+1) turn counter-clockwise by pos * theta^(-2i/64), i = 0..31,
+ *     with the base theta an argument (10000 in the original);
+ *   - token t of every sequence sits at position pos0 + t;
+ *   - lambda is one scalar per (token, signal head): sigmoid of the dot
+ *     product of x_t with row h of W^lambda [n_sig, d_model];
+ *   - the gate's projection is an ordinary matmul outside this step; the step
+ *     applies its sigmoid to the given pre-activations.
+ */
+static void rope64(const float *x, double pos, double theta, double *out)
+{
+    for (int i = 0; i < 32; ++i) {
+#if ORACLE_MUTANT == 13
+        const double freq = pow(theta, -(double)i / 64.0);
+#else
+        const double freq = pow(theta, -2.0 * i / 64.0);
+#endif
+        const double a = pos * freq;
+        const double c = cos(a);
+#if ORACLE_MUTANT == 12
+        const double s = -sin(a);
+#else
+        const double s = sin(a);
+#endif
+#if ORACLE_MUTANT == 11
+        const int i0 = i, i1 = i + 32;
+#else
+        const int i0 = 2 * i, i1 = 2 * i + 1;
+#endif
+        out[i0] = (double)x[i0] * c - (double)x[i1] * s;
+        out[i1] = (double)x[i0] * s + (double)x[i1] * c;
+    }
+}
+
+static double sigmoid(double z)
+{
+#if ORACLE_MUTANT == 14
+    return z;
+#else
+    return 1.0 / (1.0 + exp(-z));
+#endif
+}
+
+/*
+ * Rotated query heads (content part copied, rotary part rotated), the rotated
+ * shared key as it lands in each KV head's rotary part, lambda and the gate.
+ *   q_signal [B,T,n_sig,d_qk], q_noise [B,T,n_kv,d_qk], k_rope [B,T,64],
+ *   x [B,T,d_model], w_lambda [n_sig,d_model], gate_pre [B,T,n_sig,d_v]
+ * -> q_signal_out, q_noise_out (same shapes), k_rot [B,T,n_kv,64],
+ *    lambda_out [B,T,n_sig], gate_out [B,T,n_sig,d_v]   (all fp64)
+ */
+int gdla_oracle_prep(const float *q_signal, const float *q_noise, const float *k_rope,
+                     const float *x, const float *w_lambda, const float *gate_pre,
+                     int B, int T, int n_kv, int group, int d_qk, int d_v, int d_model,
+                     int pos0, double theta, double *q_signal_out, double *q_noise_out,
+                     double *k_rot, double *lambda_out, double *gate_out)
+{
+    if (B < 0 || T < 0 || n_kv < 1 || group < 1 || d_qk < 64 || d_v < 1 || d_model < 1 ||
+        pos0 < 0 || !(theta > 1.0))
+        return ORACLE_BAD_ARG;
+    const int n_sig = n_kv * group;
+    const long n_tok = (long)B * T;
+#pragma omp parallel for schedule(static)
+    for (long bt = 0; bt < n_tok; ++bt) {
+        const double pos = (double)(pos0 + bt % T);
+        /* query heads: signal then noise */
+        for (int h = 0; h < n_sig + n_kv; ++h) {
+            const float *src = h < n_sig ? q_signal + (bt * n_sig + h) * d_qk
+                                         : q_noise + (bt * n_kv + (h - n_sig)) * d_qk;
+            double *dst = h < n_sig ? q_signal_out + (bt * n_sig + h) * d_qk
+                                    : q_noise_out + (bt * n_kv + (h - n_sig)) * d_qk;
+#if ORACLE_MUTANT == 16
+            const int rot0 = 0;
+#else
+            const int rot0 = d_qk - 64;
+#endif
+            for (int d = 0; d < d_qk; ++d) dst[d] = src[d];
+            rope64(src + rot0, pos, theta, dst + rot0);
+        }
+        /* the shared key, once per KV head */
+        for (int j = 0; j < n_kv; ++j) {
+#if ORACLE_MUTANT == 15
+            if (j > 0) {
+                for (int d = 0; d < 64; ++d) k_rot[(bt * n_kv + j) * 64 + d] = k_rope[bt * 64 + d];
+                continue;
+            }
+#endif
+            rope64(k_rope + bt * 64, pos, theta, k_rot + (bt * n_kv + j) * 64);
+        }
+        /* lambda_h = sigmoid(x_t . W^lambda[h]) */
+        for (int h = 0; h < n_sig; ++h) {
+            double z = 0.0;
+            for (int k = 0; k < d_model; ++k)
+                z += (double)x[bt * d_model + k] * (double)w_lambda[(long)h * d_model + k];
+            lambda_out[bt * n_sig + h] = sigmoid(z);
+        }
+        for (long e = 0; e < (long)n_sig * d_v; ++e)
+            gate_out[bt * n_sig * d_v + e] = sigmoid((double)gate_pre[bt * n_sig * d_v + e]);
+    }
+    return ORACLE_OK;
+}
+
 /* Number of OpenMP threads a parallel region of this library would use. */
 int gdla_oracle_num_threads(void)
 {

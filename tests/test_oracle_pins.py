@@ -438,6 +438,116 @@ def test_latent_lambda1_identical_queries_give_zero():
 
 
 # ----------------------------------------------------------------------------
+# 10b. the step ahead of the attention core: rotary embedding, lambda, gate
+# ----------------------------------------------------------------------------
+
+def prep_inputs(B=1, T=3, n_kv=2, d_model=64, seed=0):
+    r = np.random.default_rng(seed)
+    f = lambda *s: r.standard_normal(s).astype(np.float32)
+    n_sig = 4 * n_kv
+    return dict(q_signal=f(B, T, n_sig, 192), q_noise=f(B, T, n_kv, 192), k_rope=f(B, T, 64),
+                x=f(B, T, d_model), w_lambda=(0.1 * f(n_sig, d_model)).astype(np.float32),
+                gate_pre=f(B, T, n_sig, 128))
+
+
+def run_prep(lib, d, **kw):
+    return oracle.prep(d["q_signal"], d["q_noise"], d["k_rope"], d["x"], d["w_lambda"], d["gate_pre"],
+                       lib=lib, **kw)
+
+
+def check_rope_closed_form(lib):
+    """Unit vectors turn by a known angle in a known plane: e_0 at position 1 by
+    1 radian in the plane of values 0, 1 (pair 0 turns at theta^0 = 1 per
+    position); e_32 at position 100 by 100 * 10000^(-32/64) = 1 radian in the
+    plane of values 32, 33 (pair 16).  Query heads carry the rotary part in
+    their last 64 values; every KV head receives the rotated shared key."""
+    d = prep_inputs(T=1)
+    for pos0, unit, plane in [(1, 0, (0, 1)), (100, 32, (32, 33))]:
+        e = dict(d)
+        e["q_signal"] = np.zeros_like(d["q_signal"])
+        e["q_signal"][..., 128 + unit] = 1.0
+        e["k_rope"] = np.zeros_like(d["k_rope"])
+        e["k_rope"][..., unit] = 1.0
+        o = run_prep(lib, e, pos0=pos0, theta=10000.0)
+        want = np.zeros(64)
+        want[plane[0]], want[plane[1]] = math.cos(1.0), math.sin(1.0)
+        np.testing.assert_allclose(o["q_signal"][0, 0, :, 128:], np.broadcast_to(want, (8, 64)), atol=1e-12)
+        np.testing.assert_allclose(o["k_rot"][0, 0], np.broadcast_to(want, (2, 64)), atol=1e-12)
+
+
+def check_rope_relative_norm_identity(lib):
+    """The defining property of the rotary embedding: the dot product of a
+    rotated query and a rotated key depends on their positions only through
+    the difference; every pair keeps its length; position 0 is the identity."""
+    d = prep_inputs(T=5, n_kv=1)
+    a = run_prep(lib, d, pos0=0, theta=10000.0)
+    b = run_prep(lib, d, pos0=37, theta=10000.0)
+    sa = np.einsum("thd,sd->ths", a["q_signal"][0, :, :, 128:], a["k_rot"][0, :, 0])
+    sb = np.einsum("thd,sd->ths", b["q_signal"][0, :, :, 128:], b["k_rot"][0, :, 0])
+    np.testing.assert_allclose(sa, sb, rtol=1e-9, atol=1e-9)
+    pairs = lambda v: np.linalg.norm(v.reshape(*v.shape[:-1], 32, 2), axis=-1)
+    np.testing.assert_allclose(pairs(b["q_noise"][..., 128:]), pairs(d["q_noise"][..., 128:].astype(np.float64)),
+                               rtol=1e-12)
+    np.testing.assert_allclose(a["q_signal"][0, 0], d["q_signal"][0, 0], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(a["k_rot"][0, 0, 0], d["k_rope"][0, 0], rtol=0, atol=1e-12)
+
+
+def check_prep_structure(lib):
+    """The content part (first 128 values) of every query head passes unchanged,
+    and every KV head receives the same rotated key."""
+    d = prep_inputs(T=4, n_kv=3)
+    o = run_prep(lib, d, pos0=9, theta=10000.0)
+    np.testing.assert_array_equal(o["q_signal"][..., :128], d["q_signal"][..., :128])
+    np.testing.assert_array_equal(o["q_noise"][..., :128], d["q_noise"][..., :128])
+    for j in range(1, 3):
+        np.testing.assert_array_equal(o["k_rot"][:, :, j], o["k_rot"][:, :, 0])
+
+
+def check_lambda_gate_sigmoid(lib):
+    """lambda = sigmoid(x . W^lambda[h]) and gate = sigmoid(pre-activation):
+    zero weights or pre-activations give exactly 1/2; negating the input gives
+    1 - value; a one-hot x picks out a single weight."""
+    d = prep_inputs(T=2)
+    o = run_prep(lib, d, pos0=0, theta=10000.0)
+    z = dict(d, w_lambda=np.zeros_like(d["w_lambda"]), gate_pre=np.zeros_like(d["gate_pre"]))
+    oz = run_prep(lib, z)
+    assert np.all(oz["lam"] == 0.5) and np.all(oz["gate"] == 0.5)
+    neg = run_prep(lib, dict(d, x=-d["x"], gate_pre=-d["gate_pre"]))
+    np.testing.assert_allclose(neg["lam"], 1.0 - o["lam"], rtol=0, atol=1e-14)
+    np.testing.assert_allclose(neg["gate"], 1.0 - o["gate"], rtol=0, atol=1e-14)
+    onehot = np.zeros_like(d["x"])
+    onehot[..., 5] = 1.0
+    oh = run_prep(lib, dict(d, x=onehot))
+    w5 = d["w_lambda"][:, 5].astype(np.float64)
+    np.testing.assert_allclose(oh["lam"][0, 0], 1.0 / (1.0 + np.exp(-w5)), rtol=1e-14)
+    assert np.all((o["lam"] > 0) & (o["lam"] < 1))
+
+
+def test_rope_closed_form():
+    check_rope_closed_form(oracle.library())
+
+
+def test_rope_relative_position_norm_identity():
+    check_rope_relative_norm_identity(oracle.library())
+
+
+def test_prep_structure():
+    check_prep_structure(oracle.library())
+
+
+def test_lambda_and_gate_are_sigmoids():
+    check_lambda_gate_sigmoid(oracle.library())
+
+
+def test_prep_rejects_bad_arguments():
+    d = prep_inputs()
+    with pytest.raises(ValueError):
+        run_prep(oracle.library(), d, pos0=-1)
+    with pytest.raises(ValueError):
+        run_prep(oracle.library(), d, theta=1.0)
+
+
+# ----------------------------------------------------------------------------
 # 11. every planted mistake fails at least one pin
 # ----------------------------------------------------------------------------
 
@@ -452,6 +562,12 @@ MUTANTS = {
     8: "latent decode: rotary key dropped",
     9: "latent decode: W_uk read transposed",
     10: "latent decode: values up-projected with W_uk",
+    11: "rotary pairs taken as halves (i, i+32) instead of adjacent values",
+    12: "rotation turned the wrong way",
+    13: "rotary frequencies theta^(-i/64) instead of theta^(-2i/64)",
+    14: "lambda and gate without the sigmoid",
+    15: "shared rotary key left unrotated in KV heads past the first",
+    16: "rotary embedding applied to the first 64 values of a head",
 }
 
 
@@ -466,6 +582,10 @@ def pin_suite(lib):
         "affine_lambda": lambda: check_affine_lambda(lib),
         "latent_expanded": lambda: check_latent_equals_expanded(lib, windows=(0, 5)),
         "latent_window_one": lambda: check_latent_window_one(lib),
+        "rope_closed_form": lambda: check_rope_closed_form(lib),
+        "rope_relative": lambda: check_rope_relative_norm_identity(lib),
+        "prep_structure": lambda: check_prep_structure(lib),
+        "lambda_gate_sigmoid": lambda: check_lambda_gate_sigmoid(lib),
     }
     failed = []
     for name, fn in checks.items():
