@@ -179,3 +179,39 @@ def decode_latent(q_signal, q_noise, latent_cache, cu_seqlens, max_seqlen_k, w_u
         out.data_ptr(), workspace.data_ptr(), workspace.numel(), B, n_kv, GROUP, D_C, D_R, D_V,
         int(window), float(scale), _stream_ptr(latent_cache.device)))
     return out
+
+
+def prep(q_signal, q_noise, k_rope, k, x, w_lambda, gate_pre, pos0=0, rope_theta=10000.0,
+         lam_out=None, gate_out=None):
+    """The step ahead of the attention core, in one launch.
+
+    Rotates the rotary part (values 128..191) of every head of q_signal
+    [B,T,4*n_kv,192] and q_noise [B,T,n_kv,192] in place, writes the rotated
+    shared key k_rope [B,T,64] into the rotary part of every KV head of k
+    [B,T,n_kv,192], and returns (lam [B,T,4*n_kv], gate [B,T,4*n_kv,128]) with
+    lam = sigmoid(x @ w_lambda^T) for x [B,T,d_model], w_lambda [4*n_kv,
+    d_model], and gate = sigmoid(gate_pre).  gate_out may be gate_pre itself.
+    Token t sits at position pos0 + t.  All bf16, enqueued on the current stream.
+    """
+    B, T, n_kv, _ = k.shape
+    n_sig = n_kv * GROUP
+    d_model = x.shape[-1]
+    _check(q_signal, "q_signal", (B, T, n_sig, D_QK))
+    _check(q_noise, "q_noise", (B, T, n_kv, D_QK))
+    _check(k_rope, "k_rope", (B, T, 64))
+    _check(k, "k", (B, T, n_kv, D_QK))
+    _check(x, "x", (B, T, d_model))
+    _check(w_lambda, "w_lambda", (n_sig, d_model))
+    _check(gate_pre, "gate_pre", (B, T, n_sig, D_V))
+    if lam_out is None:
+        lam_out = torch.empty((B, T, n_sig), dtype=torch.bfloat16, device=k.device)
+    if gate_out is None:
+        gate_out = torch.empty((B, T, n_sig, D_V), dtype=torch.bfloat16, device=k.device)
+    _check(lam_out, "lam_out", (B, T, n_sig))
+    _check(gate_out, "gate_out", (B, T, n_sig, D_V))
+    lib = _lib.load()
+    _lib.check(lib.gdla_prep(
+        q_signal.data_ptr(), q_noise.data_ptr(), k_rope.data_ptr(), k.data_ptr(), x.data_ptr(),
+        w_lambda.data_ptr(), lam_out.data_ptr(), gate_pre.data_ptr(), gate_out.data_ptr(), B, T, n_kv,
+        GROUP, D_QK, D_V, d_model, int(pos0), float(rope_theta), _stream_ptr(k.device)))
+    return lam_out, gate_out

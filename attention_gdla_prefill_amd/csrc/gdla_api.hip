@@ -241,3 +241,60 @@ extern "C" int gdla_decode_latent(const void *q_signal, const void *q_noise, con
     if (e != hipSuccess) return fail(GDLA_ERR_HIP, "latent decode launch: %s", hipGetErrorString(e));
     return GDLA_OK;
 }
+
+extern "C" int gdla_prep(void *q_signal, void *q_noise, const void *k_rope, void *k, const void *x,
+                         const void *w_lambda, void *lambda_out, const void *gate_pre, void *gate_out,
+                         int B, int T, int n_kv, int group, int d_qk, int d_v, int d_model, int pos0,
+                         float rope_theta, void *stream) {
+    g_last_error[0] = 0;
+    if (B < 0 || T < 0 || pos0 < 0)
+        return fail(GDLA_ERR_INVALID_ARG, "B, T and pos0 must be >= 0 (got %d, %d, %d)", B, T, pos0);
+    if (int rc = check_head_shape(n_kv, group, d_qk, d_v)) return rc;
+    if (d_model < 1) return fail(GDLA_ERR_INVALID_ARG, "d_model must be >= 1 (got %d)", d_model);
+    if (d_model % 32 != 0)
+        return fail(GDLA_ERR_UNSUPPORTED, "this build needs d_model to be a multiple of 32 (got %d)", d_model);
+    if (!std::isfinite(rope_theta) || !(rope_theta > 1.f))
+        return fail(GDLA_ERR_INVALID_ARG, "rope_theta must be finite and > 1 (got %g)", (double)rope_theta);
+    if ((long)pos0 + T > 2147483647L) return fail(GDLA_ERR_INVALID_ARG, "pos0 + T must be < 2^31");
+    if (B == 0 || T == 0) return GDLA_OK;
+
+    void *ptrs[9] = {q_signal, q_noise, const_cast<void *>(k_rope), k, const_cast<void *>(x),
+                     const_cast<void *>(w_lambda), lambda_out, const_cast<void *>(gate_pre), gate_out};
+    const char *names[9] = {"q_signal", "q_noise", "k_rope", "k", "x", "w_lambda", "lambda_out", "gate_pre",
+                            "gate_out"};
+    for (int i = 0; i < 9; ++i) {
+        if (!ptrs[i]) return fail(GDLA_ERR_INVALID_ARG, "%s is NULL", names[i]);
+        if (!aligned(ptrs[i], 16)) return fail(GDLA_ERR_MISALIGNED, "%s is not 16-byte aligned", names[i]);
+    }
+    const long double n_tok = (long double)B * T;
+    const long double ns = (long double)n_kv * group;
+    if (n_tok * ((long double)d_model + ns * d_qk + ns * d_v) * 2 >= 4.6e18L)
+        return fail(GDLA_ERR_INVALID_ARG, "tensor sizes exceed the 2^62-byte limit");
+    if (gdla::prep_grid_blocks((long)B * T) >= (1L << 31))
+        return fail(GDLA_ERR_INVALID_ARG, "B * T / 16 must be < 2^31");
+
+    const uintptr_t nt = (uintptr_t)B * (uintptr_t)T, s = (uintptr_t)n_kv * group;
+    auto R = [](const char *n, const void *p, uintptr_t bytes) {
+        return Range{n, (uintptr_t)p, (uintptr_t)p + bytes};
+    };
+    const Range outs[5] = {R("q_signal", q_signal, nt * s * d_qk * 2), R("q_noise", q_noise, nt * n_kv * d_qk * 2),
+                           R("k", k, nt * n_kv * d_qk * 2), R("lambda_out", lambda_out, nt * s * 2),
+                           R("gate_out", gate_out, nt * s * d_v * 2)};
+    const Range ins[4] = {R("k_rope", k_rope, nt * 64 * 2), R("x", x, nt * d_model * 2),
+                          R("w_lambda", w_lambda, s * d_model * 2), R("gate_pre", gate_pre, nt * s * d_v * 2)};
+    for (int i = 0; i < 5; ++i) {
+        for (int j = i + 1; j < 5; ++j)
+            if (overlaps(outs[i], outs[j]))
+                return fail(GDLA_ERR_INVALID_ARG, "%s overlaps %s", outs[i].name, outs[j].name);
+        for (const Range &in : ins) {
+            // the gate may be computed in place
+            if (i == 4 && in.lo == outs[4].lo && in.hi == outs[4].hi) continue;
+            if (overlaps(outs[i], in)) return fail(GDLA_ERR_INVALID_ARG, "%s overlaps %s", outs[i].name, in.name);
+        }
+    }
+
+    hipError_t e = gdla::launch_prep(q_signal, q_noise, k_rope, k, x, w_lambda, lambda_out, gate_pre, gate_out, B,
+                                     T, n_kv, d_model, pos0, rope_theta, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(GDLA_ERR_HIP, "prep launch: %s", hipGetErrorString(e));
+    return GDLA_OK;
+}

@@ -27,6 +27,11 @@ hipError_t launch_decode(const void *qs, const void *qn, const void *kc, const v
                          hipStream_t stream);
 
 // Latent-cache decode: splits per sequence, workspace bytes, launch (3 kernels).
+long prep_grid_blocks(long n_tok);
+hipError_t launch_prep(void *q_signal, void *q_noise, const void *k_rope, void *k, const void *x,
+                       const void *w_lambda, void *lambda_out, const void *gate_pre, void *gate_out,
+                       int B, int T, int n_kv, int d_model, int pos0, float rope_theta, hipStream_t stream);
+
 int latent_splits(int max_seqlen_k, int window);
 size_t latent_workspace_bytes(int B, int n_kv, int n_split);
 hipError_t launch_decode_latent(const void *qs, const void *qn, const void *lat, const int32_t *cu,

@@ -47,7 +47,7 @@ constexpr int LT_COPIES = (LT_BN + LT_BN / 8) / LT_WAVES; // 9 copy instructions
 constexpr int LT_QB = 6;                  // k-steps whose A fragments are read together
 constexpr int LT_QK_AHEAD = 6;            // A-fragment reads kept in flight ahead of their products
 static_assert(LT_KK % LT_QB == 0, "k-step batches");
-static_assert(LT_BN / 8 == LT_WAVES && LT_BN % LT_WAVES == 0, "copies split evenly over the waves");
+static_assert(LT_BN / 8 == LT_WAVES && LT_COPIES == LT_BN / LT_WAVES + 1, "copies split evenly over the waves");
 // LDS rows: the c part with a 32-byte pad (conflict-free 16-row fragment reads),
 // the rotary part packed (8 rows per copy instruction)
 constexpr int LT_CS = LT_C + 16;          // bf16 per c row in LDS (1056 bytes)

@@ -9,7 +9,9 @@ differential combine and the gate.
 Printed: ONE JSON line with the throughput (unmasked FLOPs / time), the
 roofline of the prefill kernel (timed with HIP events on the stream it runs
 on), the CPU oracle timed on a bounded sample of the same workload, and the
-other workloads (sliding-window prefill, 128K prefill, decode) under "extra".
+other workloads (sliding-window prefill, 128K prefill, prefill after a
+prefix, decode over the expanded and the latent cache, the pre-attention step)
+under "extra".
 
     python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--no-extra]
                     [--extras pf_swa_32k,dec_full,...]
@@ -155,6 +157,54 @@ def bench_prefill(name, steps, warmup):
             "tflops": flops / (kern_ms * 1e-3) / 1e12, "gbs": nbytes / (kern_ms * 1e-3) / 1e9}
 
 
+def prep_bytes(w, d_model=4096):
+    """Algorithmic HBM bytes of the pre-attention step at prefill workload w:
+    the rotary parts of the query heads read and written, the rotary key read
+    once and written into every KV head, x read, W^lambda read once, lambda
+    written, the gate's pre-activations read and the gate written."""
+    n_tok = w.B * w.T
+    return (n_tok * (w.n_sig + w.n_kv) * 64 * 2 * 2 + n_tok * 64 * 2 + n_tok * w.n_kv * 64 * 2
+            + n_tok * d_model * 2 + w.n_sig * d_model * 2 + n_tok * w.n_sig * 2
+            + n_tok * w.n_sig * w.d_v * 2 * 2)
+
+
+def bench_prep(name, steps, warmup):
+    """The pre-attention step (rotary embedding, lambda, gate) at the shapes of
+    prefill workload name, cold cache (a 512 MB buffer is rewritten before each
+    launch).  It rotates in place, so the inputs drift between launches; the
+    time does not depend on the values."""
+    import torch
+    import attention_gdla_prefill_amd as gdla
+    import workload as W
+    w = W.WORKLOADS[name]
+    d = W.prep_inputs(w, seed=0, device="cuda")
+    lam = torch.empty((w.B, w.T, w.n_sig), dtype=torch.bfloat16, device="cuda")
+    gate = torch.empty_like(d["gate_pre"])
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    call = lambda: gdla.prep(d["q_signal"], d["q_noise"], d["k_rope"], d["k"], d["x"], d["w_lambda"],
+                             d["gate_pre"], lam_out=lam, gate_out=gate)
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(steps):
+        flush.fill_(1)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        call()
+        b.record(stream)
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b))
+    ms = sorted(times)[len(times) // 2]
+    nbytes = prep_bytes(w)
+    del d, lam, gate, flush
+    torch.cuda.empty_cache()
+    return {"kernel_ms": ms, "bytes": nbytes, "gbs": nbytes / (ms * 1e-3) / 1e9,
+            "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+            "cache": "cold (512 MB buffer rewritten before each launch)"}
+
+
 def bench_decode(name, steps, warmup):
     import torch
     import attention_gdla_prefill_amd as gdla
@@ -280,7 +330,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--extras", default="pf_swa_32k,pf_full_128k,pf_prefix_4k_32k,pf_swa_rank,"
-                                        "dec_full,dec_swa,dec_latent_full,dec_latent_swa",
+                                        "dec_full,dec_swa,dec_latent_full,dec_latent_swa,prep_4k,prep_swa_32k",
                     help="comma-separated extra workloads to time (a profile of one workload "
                          "names just that one)")
     ap.add_argument("--copy-probe", action="store_true",
@@ -296,7 +346,7 @@ def main():
     wanted = [] if args.no_extra else [x for x in args.extras.split(",") if x]
     for name in wanted:
         if name not in ("pf_swa_32k", "pf_full_128k", "pf_prefix_4k_32k", "pf_swa_rank", "dec_full",
-                        "dec_swa", "dec_latent_full", "dec_latent_swa"):
+                        "dec_swa", "dec_latent_full", "dec_latent_swa", "prep_4k", "prep_swa_32k"):
             print("unknown extra workload %r" % name, file=sys.stderr)
             sys.exit(2)
 
@@ -337,6 +387,11 @@ def main():
             print("[bench] extra %s" % name, file=sys.stderr, flush=True)
             fn = bench_decode_latent if name.startswith("dec_latent") else bench_decode
             extra[name] = fn(name, 10, 2)
+        for name, shape in (("prep_4k", "pf_full_4k"), ("prep_swa_32k", "pf_swa_32k")):
+            if name not in wanted:
+                continue
+            print("[bench] extra %s" % name, file=sys.stderr, flush=True)
+            extra[name] = dict(bench_prep(shape, 20, 5), shapes=shape)
 
     peaks = measured_peaks() if args.peaks else None
 

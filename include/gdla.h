@@ -212,6 +212,46 @@ int gdla_decode_latent(const void *q_signal, const void *q_noise, const void *la
                        int B, int n_kv, int group, int d_c, int d_r, int d_v,
                        int window, float softmax_scale, void *stream);
 
+/*
+ * gdla_prep -- the step ahead of gdla_prefill / gdla_prefill_prefix, fused
+ * into one pass over the tokens (aitrends.kr, GDLA paragraph: the query path
+ * gives a content and a rotary query, the KV path a compressed KV and a
+ * decoupled rotary key, lambda_t = sigmoid(x_t W^lambda), and a query-based
+ * element-wise gate follows the subtraction; head-dimension paragraph: the
+ * rotary component is 64 values and the rotary key is shared by every KV
+ * head; metalmedia, Table 1: attention with output gating).
+ *
+ *   q_signal   [B, T, n_kv*group, d_qk]  in/out: values 128..191 of each head (the
+ *                                        rotary part) rotated in place, 0..127 untouched
+ *   q_noise    [B, T, n_kv, d_qk]        in/out, as q_signal
+ *   k_rope     [B, T, 64]                the shared rotary key before rotation
+ *   k          [B, T, n_kv, d_qk]        out: values 128..191 of every KV head receive
+ *                                        the rotated shared key; 0..127 untouched
+ *   x          [B, T, d_model]           hidden states
+ *   w_lambda   [n_kv*group, d_model]     lambda projection (row h serves signal head h)
+ *   lambda_out [B, T, n_kv*group]        out: sigmoid(x_t . w_lambda[h])
+ *   gate_pre   [B, T, n_kv*group, d_v]   the output gate's pre-activations
+ *   gate_out   [B, T, n_kv*group, d_v]   out: sigmoid(gate_pre); may be gate_pre itself
+ *   pos0       position of token 0 (token t of every sequence sits at pos0 + t;
+ *              pass P for the new tokens of gdla_prefill_prefix)
+ *   rope_theta base of the rotary frequencies (10000 in the original rotary
+ *              embedding)
+ *
+ * Rotation: the original rotary embedding on adjacent pairs, for i = 0..31
+ *     (r[2i], r[2i+1]) <- (r[2i] c - r[2i+1] s, r[2i] s + r[2i+1] c),
+ *     c, s = cos, sin(pos * rope_theta^(-2i/64));
+ * angles and their sines in fp64, the rotation in fp32, results rounded to
+ * bf16 (round to nearest even); lambda's dot products accumulate in fp32.
+ * Outputs must not overlap each other or the inputs (except gate_out ==
+ * gate_pre).  B = 0 or T = 0 is a valid empty call.  This build supports
+ * group = 4, d_qk = 192, d_v = 128 and d_model a multiple of 32; other shapes
+ * return GDLA_ERR_UNSUPPORTED.
+ */
+int gdla_prep(void *q_signal, void *q_noise, const void *k_rope, void *k, const void *x,
+              const void *w_lambda, void *lambda_out, const void *gate_pre, void *gate_out,
+              int B, int T, int n_kv, int group, int d_qk, int d_v, int d_model, int pos0,
+              float rope_theta, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

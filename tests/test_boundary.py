@@ -201,3 +201,41 @@ def test_decode_latent_rejections(lib):
     assert decode_latent(lib, ws_bytes=need - 1) == WORKSPACE
     assert decode_latent(lib, ws=A + 0x900000000 + 128, ws_bytes=need) == MISALIGNED
     assert decode_latent(lib, [None] * 8, cu=None, B=0) == OK
+
+
+def prep(lib, ptrs=None, B=1, T=64, n_kv=16, group=4, d_qk=192, d_v=128, d_model=4096, pos0=0,
+         theta=10000.0):
+    if ptrs is None:
+        ptrs = [A + i * (1 << 36) for i in range(9)]
+    return lib.gdla_prep(*ptrs, B, T, n_kv, group, d_qk, d_v, d_model, pos0, ctypes.c_float(theta), None)
+
+
+def test_prep_rejections(lib):
+    assert prep(lib, B=-1) == INVALID
+    assert prep(lib, pos0=-1) == INVALID
+    assert prep(lib, group=2) == UNSUPPORTED
+    assert prep(lib, d_model=0) == INVALID
+    assert prep(lib, d_model=100) == UNSUPPORTED
+    assert prep(lib, theta=1.0) == INVALID
+    assert prep(lib, theta=float("nan")) == INVALID
+    assert prep(lib, T=8, pos0=2147483645) == INVALID
+    for i in range(9):
+        ptrs = [A + k * (1 << 36) for k in range(9)]
+        ptrs[i] = None
+        assert prep(lib, ptrs) == INVALID
+        ptrs[i] = A + 8 + i * (1 << 36)
+        assert prep(lib, ptrs) == MISALIGNED
+    # lambda_out inside x
+    ptrs = [A + k * (1 << 36) for k in range(9)]
+    ptrs[6] = ptrs[4] + 4096
+    assert prep(lib, ptrs) == INVALID
+    assert b"overlaps" in lib.gdla_last_error()
+    # the gate may be computed in place, but not over a shifted copy of itself
+    ptrs = [A + k * (1 << 36) for k in range(9)]
+    ptrs[8] = ptrs[7] + 256
+    assert prep(lib, ptrs) == INVALID
+
+
+def test_prep_empty_is_noop(lib):
+    assert prep(lib, [None] * 9, B=0) == OK
+    assert prep(lib, [None] * 9, T=0) == OK

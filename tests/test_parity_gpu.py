@@ -381,3 +381,83 @@ def test_decode_latent_configs_sampled(name):
         compare(got[b:b + 1], want, "%s seq %d (L=%d)" % (name, b, lengths[b]))
     del d
     torch.cuda.empty_cache()
+
+
+# ----------------------------------------------------------------------------
+# the step ahead of the attention core (rotary embedding, lambda, gate)
+# ----------------------------------------------------------------------------
+
+def gpu_prep(d, pos0, theta=10000.0, in_place_gate=False):
+    """Runs the prep step on copies of the in/out tensors; returns them."""
+    import attention_gdla_prefill_amd as gdla
+    o = {k: d[k].clone() for k in ("q_signal", "q_noise", "k")}
+    gate_pre = d["gate_pre"].clone()
+    lam, gate = gdla.prep(o["q_signal"], o["q_noise"], d["k_rope"], o["k"], d["x"], d["w_lambda"], gate_pre,
+                          pos0=pos0, rope_theta=theta, gate_out=gate_pre if in_place_gate else None)
+    torch.cuda.synchronize()
+    o["lam"], o["gate"] = lam, gate
+    return o
+
+
+def assert_bf16_close(got, want, what, rel=2.0 ** -7, abs_=1e-6):
+    """One bf16 rounding step (a relative 2^-7 covers a full ulp) plus the fp32
+    arithmetic before it (abs_)."""
+    g = got.detach().double().cpu().numpy()
+    w = np.asarray(want, np.float64)
+    assert g.shape == w.shape, (g.shape, w.shape)
+    err = np.abs(g - w)
+    bound = rel * np.abs(w) + abs_
+    worst = float(np.max(err - bound)) if err.size else 0.0
+    log("%s: max_abs=%.3e max_over_bound=%.3e" % (what, float(err.max()) if err.size else 0.0, worst))
+    assert np.all(err <= bound), "%s: %d elements outside the bf16 bound" % (what, int(np.sum(err > bound)))
+
+
+def check_prep(got, d, pos0, theta=10000.0):
+    import oracle
+    f = lambda t: t.detach().float().cpu().numpy()
+    want = oracle.prep(f(d["q_signal"]), f(d["q_noise"]), f(d["k_rope"]), f(d["x"]), f(d["w_lambda"]),
+                       f(d["gate_pre"]), pos0=pos0, theta=theta)
+    # content parts pass bit for bit; the rotary parts, lambda and the gate to one bf16 step
+    for name in ("q_signal", "q_noise", "k"):
+        assert torch.equal(got[name][..., :128], d[name][..., :128]), "%s content part changed" % name
+    scale = float(d["q_signal"].float().abs().max()) * 2.0 ** -20
+    assert_bf16_close(got["q_signal"][..., 128:], want["q_signal"][..., 128:], "q_signal rotary", abs_=scale)
+    assert_bf16_close(got["q_noise"][..., 128:], want["q_noise"][..., 128:], "q_noise rotary", abs_=scale)
+    assert_bf16_close(got["k"][..., 128:], want["k_rot"], "k rotary (every KV head)", abs_=scale)
+    # lambda: fp32 dot products of d_model terms before the sigmoid
+    assert_bf16_close(got["lam"], want["lam"], "lambda", abs_=1e-4)
+    assert_bf16_close(got["gate"], want["gate"], "gate", abs_=1e-6)
+
+
+PREP_CASES = [
+    # (B, T, n_kv, d_model, pos0): one full head group at the hidden size; odd
+    # shapes; positions near the 256K context
+    (1, 37, 16, 4096, 0), (2, 20, 3, 96, 1000), (1, 5, 1, 32, 262000), (3, 17, 17, 160, 7),
+]
+
+
+@pytest.mark.parametrize("case", PREP_CASES, ids=lambda c: "B%d_T%d_kv%d_d%d_p%d" % c)
+def test_prep_matches_oracle(case):
+    B, T, n_kv, d_model, pos0 = case
+    log("prep B=%d T=%d n_kv=%d d_model=%d pos0=%d" % case)
+    w = W.Workload("prep", "prefill", B=B, T=T, n_kv=n_kv)
+    d = to_dev(W.prep_inputs(w, seed=60 + T, d_model=d_model))
+    check_prep(gpu_prep(d, pos0), d, pos0)
+
+
+def test_prep_gate_in_place_and_theta():
+    w = W.Workload("prep", "prefill", B=1, T=33, n_kv=2)
+    d = to_dev(W.prep_inputs(w, seed=5, d_model=64))
+    log("prep in place, theta 500000")
+    got = gpu_prep(d, 123, theta=500000.0, in_place_gate=True)
+    check_prep(got, d, 123, theta=500000.0)
+
+
+def test_prep_config_4k():
+    """The 4K prefill's shapes (16 KV heads, hidden size 4096), every token."""
+    w = W.WORKLOADS["pf_full_4k"]
+    log("prep at pf_full_4k shapes")
+    d = W.prep_inputs(w, seed=0, device="cuda")
+    check_prep(gpu_prep(d, 0), d, 0)
+    del d
+    torch.cuda.empty_cache()

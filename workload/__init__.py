@@ -181,3 +181,33 @@ def latent_decode_inputs(w, seed=0, device="cpu", lengths=None, q_std=None):
     out["lam"] = _bf16(torch.rand((B, w.n_sig), generator=gen, device=device))
     out["gate"] = _bf16(torch.sigmoid(_draw(gen, (B, w.n_sig, w.d_v), device, 1.0)))
     return out
+
+
+D_MODEL = 4096          # hidden dimension (Table 1)
+
+
+def prep_inputs(w, seed=0, device="cpu", d_model=D_MODEL):
+    """bf16 tensors for the step ahead of the attention core, at the shapes of
+    prefill workload ``w``.
+
+    Returns dict with q_signal [B,T,n_sig,192], q_noise [B,T,n_kv,192] (before
+    rotation, N(0,1)/sqrt(192)), k [B,T,n_kv,192] (content part N(0,1)/sqrt(192);
+    the rotary part is overwritten by the step, drawn here too), k_rope [B,T,64]
+    (the shared rotary key before rotation, N(0,1)/sqrt(192)), x [B,T,d_model]
+    (hidden states, N(0,1)), w_lambda [n_sig,d_model] (N(0,1)/sqrt(d_model), so
+    that x . w_lambda[h] is about N(0,1)) and gate_pre [B,T,n_sig,128] (N(0,1)).
+    Draw order: q_signal, q_noise, k, k_rope, x, w_lambda, gate_pre.
+    """
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    B, T = w.B, w.T
+    base = 1.0 / math.sqrt(w.d_qk)
+    out = {}
+    out["q_signal"] = _bf16(_draw(gen, (B, T, w.n_sig, w.d_qk), device, base))
+    out["q_noise"] = _bf16(_draw(gen, (B, T, w.n_kv, w.d_qk), device, base))
+    out["k"] = _bf16(_draw(gen, (B, T, w.n_kv, w.d_qk), device, base))
+    out["k_rope"] = _bf16(_draw(gen, (B, T, 64), device, base))
+    out["x"] = _bf16(_draw(gen, (B, T, d_model), device, 1.0))
+    out["w_lambda"] = _bf16(_draw(gen, (w.n_sig, d_model), device, 1.0 / math.sqrt(d_model)))
+    out["gate_pre"] = _bf16(_draw(gen, (B, T, w.n_sig, w.d_v), device, 1.0))
+    return out
