@@ -4,5 +4,5 @@ The computation lives in hand-written HIP kernels behind the C ABI of
 include/gdla.h (libgdla.so); this package is its Python binding.
 """
 from .api import (decode, decode_latent, decode_latent_workspace_size, decode_workspace_size,  # noqa: F401
-                  prefill, prefill_prefix, prep)
+                  prefill, prefill_backward, prefill_backward_workspace_size, prefill_prefix, prep)
 from ._lib import GdlaError  # noqa: F401

@@ -25,6 +25,9 @@ SIGNATURES = {
     "gdla_decode_latent_workspace_size": (ctypes.c_size_t, [_I, _I, _I, _I]),
     "gdla_decode_latent": (_I, [_P, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P, ctypes.c_size_t,
                                 _I, _I, _I, _I, _I, _I, _I, ctypes.c_float, _P]),
+    "gdla_prefill_backward_workspace_size": (ctypes.c_size_t, [_I, _I, _I]),
+    "gdla_prefill_backward": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t,
+                                   _I, _I, _I, _I, _I, _I, _I, ctypes.c_float, _P]),
     "gdla_prep": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I,
                        ctypes.c_float, _P]),
 }

@@ -215,3 +215,39 @@ def prep(q_signal, q_noise, k_rope, k, x, w_lambda, gate_pre, pos0=0, rope_theta
         w_lambda.data_ptr(), lam_out.data_ptr(), gate_pre.data_ptr(), gate_out.data_ptr(), B, T, n_kv,
         GROUP, D_QK, D_V, d_model, int(pos0), float(rope_theta), _stream_ptr(k.device)))
     return lam_out, gate_out
+
+
+def prefill_backward_workspace_size(B, T, n_kv):
+    return int(_lib.load().gdla_prefill_backward_workspace_size(B, T, n_kv))
+
+
+def prefill_backward(q_signal, q_noise, k, v, lam, gate, d_out, window=0, scale=None, workspace=None):
+    """Gradients of prefill(q_signal, q_noise, k, v, lam, gate, window, scale)
+    with respect to its six inputs, given d_out [B,T,4*n_kv,128] (the
+    gradient of a loss with respect to its output).  The forward is recomputed
+    inside.  Returns a dict of bf16 tensors keyed q_signal, q_noise, k, v, lam,
+    gate (each of its input's shape); enqueued on the current stream.  The
+    workspace (uint8 device tensor) is allocated here if not given."""
+    B, T, n_kv, _ = k.shape
+    n_sig = n_kv * GROUP
+    _check(q_signal, "q_signal", (B, T, n_sig, D_QK))
+    _check(q_noise, "q_noise", (B, T, n_kv, D_QK))
+    _check(k, "k", (B, T, n_kv, D_QK))
+    _check(v, "v", (B, T, n_kv, D_V))
+    _check(lam, "lam", (B, T, n_sig))
+    _check(gate, "gate", (B, T, n_sig, D_V))
+    _check(d_out, "d_out", (B, T, n_sig, D_V))
+    if scale is None:
+        scale = 1.0 / math.sqrt(D_QK)
+    need = prefill_backward_workspace_size(B, T, n_kv)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=k.device)
+    grads = {name: torch.empty_like(t) for name, t in
+             (("q_signal", q_signal), ("q_noise", q_noise), ("k", k), ("v", v), ("lam", lam), ("gate", gate))}
+    lib = _lib.load()
+    _lib.check(lib.gdla_prefill_backward(
+        q_signal.data_ptr(), q_noise.data_ptr(), k.data_ptr(), v.data_ptr(), lam.data_ptr(), gate.data_ptr(),
+        d_out.data_ptr(), grads["q_signal"].data_ptr(), grads["q_noise"].data_ptr(), grads["k"].data_ptr(),
+        grads["v"].data_ptr(), grads["lam"].data_ptr(), grads["gate"].data_ptr(), workspace.data_ptr(),
+        workspace.numel(), B, T, n_kv, GROUP, D_QK, D_V, int(window), float(scale), _stream_ptr(k.device)))
+    return grads

@@ -1,0 +1,428 @@
+// backward_gfx950.hip -- gradients of the GDLA attention core of a full
+// prefill with respect to its six inputs (q_signal, q_noise, k, v, lambda,
+// gate).
+//
+// The forward (aitrends.kr, GDLA paragraphs) per KV head j: signal heads
+// 4j..4j+3 and noise head j attend with K_j, V_j; D = H_S - lambda (.)
+// Repeat_4(H_N); out = gate (.) D.  With dO the gradient of the output:
+//   dgate = dO (.) D,  dD = gate (.) dO,
+//   dlambda_h = -sum_d dD_h H_N,j,   dH_S,h = dD_h,   dH_N,j = -sum_h lambda_h dD_h,
+// and for every head, with P its softmax weights and delta = rowsum(dH (.) H),
+//   dV_j += P^T dH,   dS = P (.) (dH V_j^T - delta),   dQ = scale dS K_j,
+//   dK_j += scale dS^T Q.
+// The forward is recomputed first (the pages' long-context training recomputes
+// activations operator by operator): the prefill kernel in its saving mode
+// writes H_S, H_N and each row's log2-sum-exp, so that P = exp2(scale log2(e)
+// S - lse) is rebuilt exactly in the passes below.
+//
+// Kernels (all deterministic: every output element is summed by one lane):
+//   bwd_pre_kernel   the element-wise differential/gate part, dH and delta;
+//   bwd_dkdv_kernel  per (sequence, KV head, 64-key block): wave w owns 16 keys
+//                    and walks every query tile that sees them for all 5 heads;
+//   bwd_dq_kernel    per (sequence, KV head, 64-query tile): wave w owns 16
+//                    queries and walks every key block they see, head by head.
+// Products are bf16 MFMA (16x16x32) with fp32 accumulation; operands that
+// have to be transposed come from LDS through the transposing reads.
+#include "gdla_device.h"
+#include "gdla_launch.h"
+
+namespace gdla {
+
+constexpr int BW_T = 64;                   // query tile and key block
+constexpr int BW_THREADS = 256;
+constexpr int BW_QROW = D_QK + 8;          // LDS row of a Q or K tile (bf16), padded
+constexpr int BW_VROW = D_V + 8;           // LDS row of a dH or V tile (bf16), padded
+
+struct BwdParams {
+    const __bf16 *qs, *qn, *k, *v, *lam, *gate, *dout;
+    const __bf16 *hs, *hn;                 // saved per-head outputs
+    const float *lse;                      // saved log2-sum-exp, [rows][n_sig + n_kv]
+    __bf16 *dhs, *dhn;                     // dH of the signal and noise heads
+    float *delta;                          // rowsum(dH (.) H), [rows][n_sig + n_kv]
+    __bf16 *dqs, *dqn, *dk, *dv, *dlam, *dgate;
+    int B, T, n_kv, window;
+    float scale, scale_log2;
+};
+
+typedef short bw_s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bw_s16x4 bw_lds_s16x4_t;
+
+__device__ __forceinline__ bw_s16x4 bw_read_tr16(const __bf16 *p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((bw_lds_s16x4_t *)(p));
+}
+
+// A operand of M^T for a row-major LDS matrix M (row stride rs): 16 columns
+// col0 .. col0+15 by the 32 rows row0 + {4g+e} and row0 + 16 + {4g+e} (the
+// k order of a B operand packed from two 16-row C blocks)
+__device__ __forceinline__ bf16x8 bw_tr_a(const __bf16 *m, int rs, int row0, int col0, int r, int g) {
+    const __bf16 *p = m + (row0 + 4 * g + (r >> 2)) * rs + col0 + 4 * (r & 3);
+    const bw_s16x4 v8[2] = {bw_read_tr16(p), bw_read_tr16(p + 16 * rs)};
+    return __builtin_bit_cast(bf16x8, v8);
+}
+
+// cooperative copy of n_rows rows of `cols` bf16 (a multiple of 8) from global
+// (row stride gs) into LDS (row stride ls); rows past n_valid are zero
+__device__ __forceinline__ void bw_load_tile(__bf16 *lds, int ls, const __bf16 *src, long gs, int n_valid,
+                                             int cols) {
+    const int cpr = cols / 8;
+    for (int i = threadIdx.x; i < BW_T * cpr; i += BW_THREADS) {
+        const int row = i / cpr, c = (i % cpr) * 8;
+        u32x4 w = {0, 0, 0, 0};
+        if (row < n_valid) w = ldg16(src + row * gs + c);
+        *reinterpret_cast<u32x4 *>(lds + row * ls + c) = w;
+    }
+}
+
+__device__ __forceinline__ bool bw_visible(int q, int key, int T, int window) {
+    return q < T && key <= q && (window == 0 || q - key < window);
+}
+
+// ---- 1. element-wise part.  32 lanes per (token, KV head j), 4 values each.
+__global__ __launch_bounds__(BW_THREADS) void bwd_pre_kernel(BwdParams p) {
+    const int lane32 = threadIdx.x & 31;
+    const long unit = (long)blockIdx.x * (BW_THREADS / 32) + (threadIdx.x >> 5);
+    const long n_units = (long)p.B * p.T * p.n_kv;
+    if (unit >= n_units) return;                 // whole 32-lane groups leave together
+    const int n_sig = p.n_kv * GROUP, n_h = n_sig + p.n_kv;
+    const long tok = unit / p.n_kv;
+    const int j = (int)(unit % p.n_kv), d0 = 4 * lane32;
+    auto ld4 = [](const __bf16 *q, float f[4]) {
+        const u32x2 w = *reinterpret_cast<const u32x2 *>(q);
+        f[0] = bf16_lo(w[0]); f[1] = bf16_hi(w[0]); f[2] = bf16_lo(w[1]); f[3] = bf16_hi(w[1]);
+    };
+    float hn[4], dhn[4] = {0.f, 0.f, 0.f, 0.f};
+    ld4(p.hn + (tok * p.n_kv + j) * D_V + d0, hn);
+    float red[2 * GROUP + 1];                    // dlambda_h, delta_h (signal), delta (noise)
+#pragma unroll
+    for (int h = 0; h < GROUP; ++h) {
+        const long row = (tok * n_sig + GROUP * j + h) * D_V + d0;
+        float o[4], gt[4], hs[4];
+        ld4(p.dout + row, o);
+        ld4(p.gate + row, gt);
+        ld4(p.hs + row, hs);
+        const float lam = (float)p.lam[tok * n_sig + GROUP * j + h];
+        float dd[4], dg[4], dl = 0.f, de = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            dd[e] = gt[e] * o[e];
+            dg[e] = o[e] * fmaf(-lam, hn[e], hs[e]);
+            dl -= dd[e] * hn[e];
+            dhn[e] -= lam * dd[e];
+        }
+        const u32x2 ddw = {pack_bf16x2(dd[0], dd[1]), pack_bf16x2(dd[2], dd[3])};
+        *reinterpret_cast<u32x2 *>(p.dhs + row) = ddw;
+        *reinterpret_cast<u32x2 *>(p.dgate + row) = u32x2{pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3])};
+        // delta from the dH the products below use (bf16)
+        de = bf16_lo(ddw[0]) * hs[0] + bf16_hi(ddw[0]) * hs[1] + bf16_lo(ddw[1]) * hs[2] + bf16_hi(ddw[1]) * hs[3];
+        red[h] = dl;
+        red[GROUP + h] = de;
+    }
+    const u32x2 dnw = {pack_bf16x2(dhn[0], dhn[1]), pack_bf16x2(dhn[2], dhn[3])};
+    *reinterpret_cast<u32x2 *>(p.dhn + (tok * p.n_kv + j) * D_V + d0) = dnw;
+    red[2 * GROUP] = bf16_lo(dnw[0]) * hn[0] + bf16_hi(dnw[0]) * hn[1] + bf16_lo(dnw[1]) * hn[2] +
+                     bf16_hi(dnw[1]) * hn[3];
+#pragma unroll
+    for (int i = 0; i < 2 * GROUP + 1; ++i)
+#pragma unroll
+        for (int o = 16; o >= 1; o >>= 1) red[i] += __shfl_xor(red[i], o);
+    if (lane32 == 0) {
+#pragma unroll
+        for (int h = 0; h < GROUP; ++h) {
+            p.dlam[tok * n_sig + GROUP * j + h] = (__bf16)red[h];
+            p.delta[tok * n_h + GROUP * j + h] = red[GROUP + h];
+        }
+        p.delta[tok * n_h + n_sig + j] = red[2 * GROUP];
+    }
+}
+
+// head h of group j (0..3 signal, 4 noise): its query rows, dH rows and column
+// in lse / delta
+struct BwHead {
+    const __bf16 *q, *dh;
+    long q_stride, dh_stride;    // elements between consecutive tokens
+    int col;
+};
+__device__ __forceinline__ BwHead bw_head(const BwdParams &p, int b, int j, int h) {
+    const int n_sig = p.n_kv * GROUP;
+    BwHead x;
+    const long tok0 = (long)b * p.T;
+    if (h < GROUP) {
+        x.q = p.qs + (tok0 * n_sig + GROUP * j + h) * D_QK;
+        x.dh = p.dhs + (tok0 * n_sig + GROUP * j + h) * D_V;
+        x.q_stride = (long)n_sig * D_QK;
+        x.dh_stride = (long)n_sig * D_V;
+        x.col = GROUP * j + h;
+    } else {
+        x.q = p.qn + (tok0 * p.n_kv + j) * D_QK;
+        x.dh = p.dhn + (tok0 * p.n_kv + j) * D_V;
+        x.q_stride = (long)p.n_kv * D_QK;
+        x.dh_stride = (long)p.n_kv * D_V;
+        x.col = n_sig + j;
+    }
+    return x;
+}
+
+// ---- 2. dK, dV.  Workgroup (64-key block, KV head j, sequence b); wave w owns
+// keys kb0 + 16w .. +15.  In C layout lane (r, g) holds element
+// [query 16qb + 4g + e][key r] of S, P, dP, dS.
+__global__ __launch_bounds__(BW_THREADS) void bwd_dkdv_kernel(BwdParams p) {
+    __shared__ __attribute__((aligned(16))) __bf16 Qs[BW_T * BW_QROW];
+    __shared__ __attribute__((aligned(16))) __bf16 Hs[BW_T * BW_VROW];
+    __shared__ float lse_s[BW_T], dl_s[BW_T];
+    const int kb0 = blockIdx.x * BW_T, j = blockIdx.y, b = blockIdx.z;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, r = lane & 15, g = lane >> 4;
+    const int n_h = p.n_kv * HEADS, T = p.T;
+    const int key = kb0 + 16 * wave + r;
+    const long kvrow = ((long)b * T + (key < T ? key : 0)) * p.n_kv + j;
+    // B operands K_w^T (lane: K[key r][32kk + 8g ..]) and V_w^T
+    bf16x8 kf[D_QK / 32], vf[D_V / 32];
+    {
+        const u32x4 z = {0, 0, 0, 0};
+#pragma unroll
+        for (int kk = 0; kk < D_QK / 32; ++kk)
+            kf[kk] = __builtin_bit_cast(bf16x8, key < T ? ldg16(p.k + kvrow * D_QK + 32 * kk + 8 * g) : z);
+#pragma unroll
+        for (int kk = 0; kk < D_V / 32; ++kk)
+            vf[kk] = __builtin_bit_cast(bf16x8, key < T ? ldg16(p.v + kvrow * D_V + 32 * kk + 8 * g) : z);
+    }
+    f32x4 dv[D_V / 16], dk[D_QK / 16];
+#pragma unroll
+    for (int i = 0; i < D_V / 16; ++i) dv[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < D_QK / 16; ++i) dk[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+
+    // query tiles that see a key of this block
+    const int qt_lo = kb0 / BW_T;
+    int qt_hi = (T - 1) / BW_T;
+    if (p.window > 0) qt_hi = min(qt_hi, (kb0 + BW_T - 1 + p.window - 1) / BW_T);
+    for (int qt = qt_lo; qt <= qt_hi; ++qt) {
+        const int q0 = qt * BW_T, n_valid = min(BW_T, T - q0);
+        for (int h = 0; h < HEADS; ++h) {
+            const BwHead hd = bw_head(p, b, j, h);
+            __syncthreads();                          // the previous tile is consumed
+            bw_load_tile(Qs, BW_QROW, hd.q + (long)q0 * hd.q_stride, hd.q_stride, n_valid, D_QK);
+            bw_load_tile(Hs, BW_VROW, hd.dh + (long)q0 * hd.dh_stride, hd.dh_stride, n_valid, D_V);
+            if (tid < BW_T) {
+                const long row = (long)b * T + q0 + tid;
+                lse_s[tid] = tid < n_valid ? p.lse[row * n_h + hd.col] : 0.f;
+                dl_s[tid] = tid < n_valid ? p.delta[row * n_h + hd.col] : 0.f;
+            }
+            __syncthreads();
+            // S = Q K_w^T and dP = dH V_w^T, four 16-query blocks
+            f32x4 s[4], dp[4];
+#pragma unroll
+            for (int qb = 0; qb < 4; ++qb) {
+                const __bf16 *qa = Qs + (16 * qb + r) * BW_QROW + 8 * g;
+                const __bf16 *ha = Hs + (16 * qb + r) * BW_VROW + 8 * g;
+                s[qb] = zero4;
+                dp[qb] = zero4;
+#pragma unroll
+                for (int kk = 0; kk < D_QK / 32; ++kk)
+                    s[qb] = mfma16(*reinterpret_cast<const bf16x8 *>(qa + 32 * kk), kf[kk], s[qb]);
+#pragma unroll
+                for (int kk = 0; kk < D_V / 32; ++kk)
+                    dp[qb] = mfma16(*reinterpret_cast<const bf16x8 *>(ha + 32 * kk), vf[kk], dp[qb]);
+            }
+            // P and dS; packed as B operands over query pairs (blocks 2i, 2i+1)
+            uint32_t pw[4][2], sw[4][2];
+#pragma unroll
+            for (int qb = 0; qb < 4; ++qb) {
+                float pv[4], dsv[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int ql = 16 * qb + 4 * g + e;
+                    const bool vis = bw_visible(q0 + ql, key, T, p.window) && key < T;
+                    pv[e] = vis ? fast_exp2(fmaf(s[qb][e], p.scale_log2, -lse_s[ql])) : 0.f;
+                    dsv[e] = pv[e] * (dp[qb][e] - dl_s[ql]);
+                }
+                pw[qb][0] = pack_bf16x2(pv[0], pv[1]);
+                pw[qb][1] = pack_bf16x2(pv[2], pv[3]);
+                sw[qb][0] = pack_bf16x2(dsv[0], dsv[1]);
+                sw[qb][1] = pack_bf16x2(dsv[2], dsv[3]);
+            }
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const bf16x8 pb = __builtin_bit_cast(bf16x8, (u32x4{pw[2 * i][0], pw[2 * i][1], pw[2 * i + 1][0],
+                                                                    pw[2 * i + 1][1]}));
+                const bf16x8 sb = __builtin_bit_cast(bf16x8, (u32x4{sw[2 * i][0], sw[2 * i][1], sw[2 * i + 1][0],
+                                                                    sw[2 * i + 1][1]}));
+                // dV^T += dH^T P, dK^T += Q^T dS over the 32 queries of pair i
+#pragma unroll
+                for (int db = 0; db < D_V / 16; ++db) dv[db] = mfma16(bw_tr_a(Hs, BW_VROW, 32 * i, 16 * db, r, g), pb, dv[db]);
+#pragma unroll
+                for (int db = 0; db < D_QK / 16; ++db) dk[db] = mfma16(bw_tr_a(Qs, BW_QROW, 32 * i, 16 * db, r, g), sb, dk[db]);
+            }
+        }
+    }
+    // lane (r, g) holds dV[key r][16db + 4g + e] and dK[key r][16db + 4g + e] / scale
+    if (key < T) {
+#pragma unroll
+        for (int db = 0; db < D_V / 16; ++db)
+            *reinterpret_cast<u32x2 *>(p.dv + kvrow * D_V + 16 * db + 4 * g) =
+                u32x2{pack_bf16x2(dv[db][0], dv[db][1]), pack_bf16x2(dv[db][2], dv[db][3])};
+#pragma unroll
+        for (int db = 0; db < D_QK / 16; ++db)
+            *reinterpret_cast<u32x2 *>(p.dk + kvrow * D_QK + 16 * db + 4 * g) =
+                u32x2{pack_bf16x2(dk[db][0] * p.scale, dk[db][1] * p.scale),
+                      pack_bf16x2(dk[db][2] * p.scale, dk[db][3] * p.scale)};
+    }
+}
+
+// ---- 3. dQ.  Workgroup (64-query tile, KV head j, sequence b); wave w owns
+// queries q0 + 16w .. +15.  In C layout lane (r, g) holds element
+// [key 16kb + 4g + e][query r] of S^T, P^T, dP^T, dS^T.
+__global__ __launch_bounds__(BW_THREADS) void bwd_dq_kernel(BwdParams p) {
+    __shared__ __attribute__((aligned(16))) __bf16 Ks[BW_T * BW_QROW];
+    __shared__ __attribute__((aligned(16))) __bf16 Vs[BW_T * BW_VROW];
+    const int q0 = blockIdx.x * BW_T, j = blockIdx.y, b = blockIdx.z;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, r = lane & 15, g = lane >> 4;
+    const int n_h = p.n_kv * HEADS, T = p.T;
+    const int q = q0 + 16 * wave + r;
+    const bool q_ok = q < T;
+    const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+    const int kb_lo = p.window > 0 ? max(0, q0 - p.window + 1) / BW_T : 0;
+    const int kb_hi = (min(q0 + BW_T, T) - 1) / BW_T;
+    const __bf16 *kseq = p.k + ((long)b * T * p.n_kv + j) * D_QK;
+    const __bf16 *vseq = p.v + ((long)b * T * p.n_kv + j) * D_V;
+    const long kv_qs = (long)p.n_kv * D_QK, kv_vs = (long)p.n_kv * D_V;
+
+    for (int h = 0; h < HEADS; ++h) {
+        const BwHead hd = bw_head(p, b, j, h);
+        // B operands Q_w^T and dH_w^T (lane: row q, values 32kk + 8g ..)
+        bf16x8 qf[D_QK / 32], hf[D_V / 32];
+        {
+            const u32x4 z = {0, 0, 0, 0};
+            const long qi = q_ok ? q : 0;
+#pragma unroll
+            for (int kk = 0; kk < D_QK / 32; ++kk)
+                qf[kk] = __builtin_bit_cast(bf16x8, q_ok ? ldg16(hd.q + qi * hd.q_stride + 32 * kk + 8 * g) : z);
+#pragma unroll
+            for (int kk = 0; kk < D_V / 32; ++kk)
+                hf[kk] = __builtin_bit_cast(bf16x8, q_ok ? ldg16(hd.dh + qi * hd.dh_stride + 32 * kk + 8 * g) : z);
+        }
+        const long row = (long)b * T + (q_ok ? q : 0);
+        const float lse = q_ok ? p.lse[row * n_h + hd.col] : 0.f;
+        const float dl = q_ok ? p.delta[row * n_h + hd.col] : 0.f;
+        f32x4 dq[D_QK / 16];
+#pragma unroll
+        for (int i = 0; i < D_QK / 16; ++i) dq[i] = zero4;
+        for (int kb = kb_lo; kb <= kb_hi; ++kb) {
+            const int k0 = kb * BW_T, n_valid = min(BW_T, T - k0);
+            __syncthreads();
+            bw_load_tile(Ks, BW_QROW, kseq + (long)k0 * kv_qs, kv_qs, n_valid, D_QK);
+            bw_load_tile(Vs, BW_VROW, vseq + (long)k0 * kv_vs, kv_vs, n_valid, D_V);
+            __syncthreads();
+            uint32_t sw[4][2];
+#pragma unroll
+            for (int k4 = 0; k4 < 4; ++k4) {
+                const __bf16 *ka = Ks + (16 * k4 + r) * BW_QROW + 8 * g;
+                const __bf16 *va = Vs + (16 * k4 + r) * BW_VROW + 8 * g;
+                f32x4 st = zero4, dpt = zero4;
+#pragma unroll
+                for (int kk = 0; kk < D_QK / 32; ++kk)
+                    st = mfma16(*reinterpret_cast<const bf16x8 *>(ka + 32 * kk), qf[kk], st);
+#pragma unroll
+                for (int kk = 0; kk < D_V / 32; ++kk)
+                    dpt = mfma16(*reinterpret_cast<const bf16x8 *>(va + 32 * kk), hf[kk], dpt);
+                float dsv[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int key = k0 + 16 * k4 + 4 * g + e;
+                    const bool vis = bw_visible(q, key, T, p.window);
+                    const float pv = vis ? fast_exp2(fmaf(st[e], p.scale_log2, -lse)) : 0.f;
+                    dsv[e] = pv * (dpt[e] - dl);
+                }
+                sw[k4][0] = pack_bf16x2(dsv[0], dsv[1]);
+                sw[k4][1] = pack_bf16x2(dsv[2], dsv[3]);
+            }
+            // dQ^T += K^T dS^T over the key pairs (blocks 2i, 2i+1)
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const bf16x8 sb = __builtin_bit_cast(bf16x8, (u32x4{sw[2 * i][0], sw[2 * i][1], sw[2 * i + 1][0],
+                                                                    sw[2 * i + 1][1]}));
+#pragma unroll
+                for (int db = 0; db < D_QK / 16; ++db) dq[db] = mfma16(bw_tr_a(Ks, BW_QROW, 32 * i, 16 * db, r, g), sb, dq[db]);
+            }
+        }
+        // lane (r, g) holds dQ[query r][16db + 4g + e] / scale
+        if (q_ok) {
+            __bf16 *dst = h < GROUP ? p.dqs + (((long)b * T + q) * (p.n_kv * GROUP) + GROUP * j + h) * D_QK
+                                    : p.dqn + (((long)b * T + q) * p.n_kv + j) * D_QK;
+#pragma unroll
+            for (int db = 0; db < D_QK / 16; ++db)
+                *reinterpret_cast<u32x2 *>(dst + 16 * db + 4 * g) =
+                    u32x2{pack_bf16x2(dq[db][0] * p.scale, dq[db][1] * p.scale),
+                          pack_bf16x2(dq[db][2] * p.scale, dq[db][3] * p.scale)};
+        }
+    }
+}
+
+// workspace: saved H_S | H_N | lse | the recomputed output | dH_S | dH_N | delta
+struct BwLayout {
+    size_t hs, hn, lse, out, dhs, dhn, delta, total;
+};
+static BwLayout bw_layout(int B, int T, int n_kv) {
+    auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    const size_t rows = (size_t)B * T, n_sig = (size_t)n_kv * GROUP;
+    BwLayout l;
+    l.hs = 0;
+    l.hn = l.hs + up(rows * n_sig * D_V * 2);
+    l.lse = l.hn + up(rows * n_kv * D_V * 2);
+    l.out = l.lse + up(rows * (n_sig + n_kv) * 4);
+    l.dhs = l.out + up(rows * n_sig * D_V * 2);
+    l.dhn = l.dhs + up(rows * n_sig * D_V * 2);
+    l.delta = l.dhn + up(rows * n_kv * D_V * 2);
+    l.total = l.delta + up(rows * (n_sig + n_kv) * 4);
+    return l;
+}
+
+size_t backward_workspace_bytes(int B, int T, int n_kv) { return bw_layout(B, T, n_kv).total; }
+
+hipError_t launch_backward(const void *qs, const void *qn, const void *k, const void *v, const void *lam,
+                           const void *gate, const void *dout, void *dqs, void *dqn, void *dk, void *dv,
+                           void *dlam, void *dgate, void *workspace, int B, int T, int n_kv, int window,
+                           float scale, hipStream_t stream) {
+    const BwLayout lay = bw_layout(B, T, n_kv);
+    char *ws = static_cast<char *>(workspace);
+    // 1. the forward again, saving H_S, H_N and the log2-sum-exp
+    hipError_t e = launch_prefill(qs, qn, k, v, lam, gate, ws + lay.out, B, T, 0, n_kv, window, scale, stream,
+                                  ws + lay.hs, ws + lay.hn, reinterpret_cast<float *>(ws + lay.lse));
+    if (e != hipSuccess) return e;
+    BwdParams p;
+    p.qs = static_cast<const __bf16 *>(qs);
+    p.qn = static_cast<const __bf16 *>(qn);
+    p.k = static_cast<const __bf16 *>(k);
+    p.v = static_cast<const __bf16 *>(v);
+    p.lam = static_cast<const __bf16 *>(lam);
+    p.gate = static_cast<const __bf16 *>(gate);
+    p.dout = static_cast<const __bf16 *>(dout);
+    p.hs = reinterpret_cast<const __bf16 *>(ws + lay.hs);
+    p.hn = reinterpret_cast<const __bf16 *>(ws + lay.hn);
+    p.lse = reinterpret_cast<const float *>(ws + lay.lse);
+    p.dhs = reinterpret_cast<__bf16 *>(ws + lay.dhs);
+    p.dhn = reinterpret_cast<__bf16 *>(ws + lay.dhn);
+    p.delta = reinterpret_cast<float *>(ws + lay.delta);
+    p.dqs = static_cast<__bf16 *>(dqs);
+    p.dqn = static_cast<__bf16 *>(dqn);
+    p.dk = static_cast<__bf16 *>(dk);
+    p.dv = static_cast<__bf16 *>(dv);
+    p.dlam = static_cast<__bf16 *>(dlam);
+    p.dgate = static_cast<__bf16 *>(dgate);
+    p.B = B;
+    p.T = T;
+    p.n_kv = n_kv;
+    p.window = window >= T ? 0 : window;
+    p.scale = scale;
+    p.scale_log2 = scale * LOG2E;
+    const long units = (long)B * T * n_kv;
+    hipLaunchKernelGGL(bwd_pre_kernel, dim3((unsigned)((units + 7) / 8)), dim3(BW_THREADS), 0, stream, p);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const unsigned n_t = (unsigned)((T + BW_T - 1) / BW_T);
+    hipLaunchKernelGGL(bwd_dkdv_kernel, dim3(n_t, n_kv, B), dim3(BW_THREADS), 0, stream, p);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(bwd_dq_kernel, dim3(n_t, n_kv, B), dim3(BW_THREADS), 0, stream, p);
+    return hipGetLastError();
+}
+
+}  // namespace gdla

@@ -298,3 +298,68 @@ extern "C" int gdla_prep(void *q_signal, void *q_noise, const void *k_rope, void
     if (e != hipSuccess) return fail(GDLA_ERR_HIP, "prep launch: %s", hipGetErrorString(e));
     return GDLA_OK;
 }
+
+extern "C" size_t gdla_prefill_backward_workspace_size(int B, int T, int n_kv) {
+    if (B < 0 || T < 0 || n_kv < 1) return 0;
+    return gdla::backward_workspace_bytes(B, T, n_kv);
+}
+
+extern "C" int gdla_prefill_backward(const void *q_signal, const void *q_noise, const void *k, const void *v,
+                                     const void *lambda_, const void *gate, const void *d_out, void *dq_signal,
+                                     void *dq_noise, void *dk, void *dv, void *dlambda, void *dgate,
+                                     void *workspace, size_t workspace_bytes, int B, int T, int n_kv, int group,
+                                     int d_qk, int d_v, int window, float softmax_scale, void *stream) {
+    g_last_error[0] = 0;
+    if (B < 0 || T < 0) return fail(GDLA_ERR_INVALID_ARG, "B and T must be >= 0 (got %d, %d)", B, T);
+    if (int rc = check_head_shape(n_kv, group, d_qk, d_v)) return rc;
+    if (int rc = check_scale_window(softmax_scale, window)) return rc;
+    if (B == 0 || T == 0) return GDLA_OK;
+    if (B > 65535 || n_kv > 65535) return fail(GDLA_ERR_INVALID_ARG, "B and n_kv must be <= 65535");
+
+    const void *ptrs[13] = {q_signal, q_noise, k, v, lambda_, gate, d_out, dq_signal, dq_noise, dk, dv, dlambda,
+                            dgate};
+    const char *names[13] = {"q_signal", "q_noise", "k", "v", "lambda", "gate", "d_out", "dq_signal", "dq_noise",
+                             "dk", "dv", "dlambda", "dgate"};
+    for (int i = 0; i < 13; ++i) {
+        if (!ptrs[i]) return fail(GDLA_ERR_INVALID_ARG, "%s is NULL", names[i]);
+        if (!aligned(ptrs[i], 16)) return fail(GDLA_ERR_MISALIGNED, "%s is not 16-byte aligned", names[i]);
+    }
+    const long double ns = (long double)n_kv * group;
+    if ((long double)B * T * ns * d_qk * 2 >= 4.6e18L)
+        return fail(GDLA_ERR_INVALID_ARG, "tensor sizes exceed the 2^62-byte limit");
+    if ((long double)T >= 2147483647.0L - 64) return fail(GDLA_ERR_INVALID_ARG, "T must be < 2^31 - 64");
+    if (gdla::prefill_grid_blocks(B, T, 0, n_kv) >= (1L << 31))
+        return fail(GDLA_ERR_INVALID_ARG, "B * n_kv * (query tiles) must be < 2^31");
+    if (((long double)T + 64) * n_kv * d_qk * 2 >= 2147483648.0L)
+        return fail(GDLA_ERR_UNSUPPORTED, "one sequence's K rows must span < 2^31 bytes ((T+64)*n_kv*d_qk*2)");
+    const size_t need = gdla::backward_workspace_bytes(B, T, n_kv);
+    if (!workspace) return fail(GDLA_ERR_WORKSPACE, "workspace is NULL, %zu bytes needed", need);
+    if (workspace_bytes < need)
+        return fail(GDLA_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
+    if (!aligned(workspace, 256)) return fail(GDLA_ERR_MISALIGNED, "workspace is not 256-byte aligned");
+
+    const uintptr_t rows = (uintptr_t)B * (uintptr_t)T, s = (uintptr_t)n_kv * group;
+    auto R = [](const char *n, const void *p, uintptr_t bytes) {
+        return Range{n, (uintptr_t)p, (uintptr_t)p + bytes};
+    };
+    const Range ins[7] = {R("q_signal", q_signal, rows * s * d_qk * 2), R("q_noise", q_noise, rows * n_kv * d_qk * 2),
+                          R("k", k, rows * n_kv * d_qk * 2), R("v", v, rows * n_kv * d_v * 2),
+                          R("lambda", lambda_, rows * s * 2), R("gate", gate, rows * s * d_v * 2),
+                          R("d_out", d_out, rows * s * d_v * 2)};
+    const Range outs[7] = {R("dq_signal", dq_signal, rows * s * d_qk * 2),
+                           R("dq_noise", dq_noise, rows * n_kv * d_qk * 2), R("dk", dk, rows * n_kv * d_qk * 2),
+                           R("dv", dv, rows * n_kv * d_v * 2), R("dlambda", dlambda, rows * s * 2),
+                           R("dgate", dgate, rows * s * d_v * 2), R("workspace", workspace, need)};
+    for (int i = 0; i < 7; ++i) {
+        for (int j = i + 1; j < 7; ++j)
+            if (overlaps(outs[i], outs[j])) return fail(GDLA_ERR_INVALID_ARG, "%s overlaps %s", outs[i].name, outs[j].name);
+        for (const Range &in : ins)
+            if (overlaps(outs[i], in)) return fail(GDLA_ERR_INVALID_ARG, "%s overlaps %s", outs[i].name, in.name);
+    }
+
+    hipError_t e = gdla::launch_backward(q_signal, q_noise, k, v, lambda_, gate, d_out, dq_signal, dq_noise, dk, dv,
+                                         dlambda, dgate, workspace, B, T, n_kv, window, softmax_scale,
+                                         static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(GDLA_ERR_HIP, "backward launch: %s", hipGetErrorString(e));
+    return GDLA_OK;
+}

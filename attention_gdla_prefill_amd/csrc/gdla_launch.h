@@ -10,9 +10,12 @@
 namespace gdla {
 
 // Prefill of Tq query rows per sequence at positions P .. P+Tq-1 over P+Tq key rows.
+// save_hs / save_hn / save_lse non-null (with P = 0): also write the per-head
+// outputs and the log2-sum-exp of every head's softmax row
 hipError_t launch_prefill(const void *qs, const void *qn, const void *k, const void *v,
                           const void *lam, const void *gate, void *out, int B, int Tq, int P, int n_kv,
-                          int window, float scale, hipStream_t stream);
+                          int window, float scale, hipStream_t stream, void *save_hs = nullptr,
+                          void *save_hn = nullptr, float *save_lse = nullptr);
 // Query tiles of one (sequence, KV head) times B * n_kv.
 long prefill_grid_blocks(int B, int Tq, int P, int n_kv);
 
@@ -27,6 +30,12 @@ hipError_t launch_decode(const void *qs, const void *qn, const void *kc, const v
                          hipStream_t stream);
 
 // Latent-cache decode: splits per sequence, workspace bytes, launch (3 kernels).
+size_t backward_workspace_bytes(int B, int T, int n_kv);
+hipError_t launch_backward(const void *qs, const void *qn, const void *k, const void *v, const void *lam,
+                           const void *gate, const void *dout, void *dqs, void *dqn, void *dk, void *dv,
+                           void *dlam, void *dgate, void *workspace, int B, int T, int n_kv, int window,
+                           float scale, hipStream_t stream);
+
 long prep_grid_blocks(long n_tok);
 hipError_t launch_prep(void *q_signal, void *q_noise, const void *k_rope, void *k, const void *x,
                        const void *w_lambda, void *lambda_out, const void *gate_pre, void *gate_out,

@@ -92,6 +92,8 @@ __device__ __forceinline__ s16x4 lds_read_tr16(const __bf16 *p) {
 struct PrefillParams {
     const __bf16 *qs, *qn, *k, *v, *lam, *gate;
     __bf16 *out;
+    __bf16 *hs, *hn;                  // saving mode: the per-head outputs H_S [rows][n_sig][D_V], H_N [rows][n_kv][D_V]
+    float *lse;                       // saving mode: log2 of each head's softmax sum, [rows][n_sig + n_kv]
     int B, n_kv, window;
     int Tq;                           // query rows per sequence (positions P .. P+Tq-1)
     int P;                            // keys before the first query (a prefix already in K/V)
@@ -131,7 +133,9 @@ __device__ __forceinline__ bool work_item(const WorkList &w, int round, int n_ru
 
 // PREFIX: queries start after a prefix of keys (P > 0); the P = 0 instance
 // folds the position offsets away.
-template <bool PREFIX>
+// TRAIN: also save what the backward needs (the per-head outputs and the
+// log2-sum-exp of every head's row, reference included).
+template <bool PREFIX, bool TRAIN>
 __global__ __launch_bounds__(PF_THREADS, 1) void prefill_kernel(PrefillParams p) {
     // ring of three K and three V tile slots: key tile t lives in slot t % 3
     __shared__ __attribute__((aligned(16))) __bf16 Kring[3][PF_BN * KS_ROW];
@@ -500,6 +504,24 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_kernel(PrefillParams p)
                     }
                     *reinterpret_cast<u32x2 *>(p.out + (row * n_sig + GROUP * j + h) * D_V + c) =
                         u32x2{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
+                    if constexpr (TRAIN)
+                        *reinterpret_cast<u32x2 *>(p.hs + (row * n_sig + GROUP * j + h) * D_V + c) =
+                            u32x2{pack_bf16x2(o[h][cb][0] * inv[h], o[h][cb][1] * inv[h]),
+                                  pack_bf16x2(o[h][cb][2] * inv[h], o[h][cb][3] * inv[h])};
+                }
+                if constexpr (TRAIN)
+                    *reinterpret_cast<u32x2 *>(p.hn + (row * n_kv + j) * D_V + c) =
+                        u32x2{pack_bf16x2(hn[0], hn[1]), pack_bf16x2(hn[2], hn[3])};
+            }
+            if constexpr (TRAIN) {
+                // the weights were exp2(score * scale * log2(e) - m_ref) with sum 1/inv
+                if (g == 0) {
+#pragma unroll
+                    for (int h = 0; h < HEADS; ++h) {
+                        const float m = m_ref[h] == -INFINITY ? 0.f : m_ref[h];
+                        const int col = h < GROUP ? GROUP * j + h : n_sig + j;
+                        p.lse[row * (n_sig + n_kv) + col] = m - __log2f(inv[h]);
+                    }
                 }
             }
         }
@@ -536,8 +558,12 @@ static int compute_units() {
 
 hipError_t launch_prefill(const void *qs, const void *qn, const void *k, const void *v,
                           const void *lam, const void *gate, void *out, int B, int Tq, int P, int n_kv,
-                          int window, float scale, hipStream_t stream) {
+                          int window, float scale, hipStream_t stream, void *save_hs, void *save_hn,
+                          float *save_lse) {
     PrefillParams p;
+    p.hs = static_cast<__bf16 *>(save_hs);
+    p.hn = static_cast<__bf16 *>(save_hn);
+    p.lse = save_lse;
     p.qs = static_cast<const __bf16 *>(qs);
     p.qn = static_cast<const __bf16 *>(qn);
     p.k = static_cast<const __bf16 *>(k);
@@ -565,10 +591,12 @@ hipError_t launch_prefill(const void *qs, const void *qn, const void *k, const v
     // one persistent workgroup per CU (at most one fits: LDS and registers)
     const long items = (long)B * n_kv * p.n_runs;
     const long blocks = std::min(items, (long)n_cu);
-    if (P > 0)
-        hipLaunchKernelGGL(prefill_kernel<true>, dim3((unsigned)blocks), dim3(PF_THREADS), 0, stream, p);
+    if (save_hs)        // the saving mode (a full prefill only)
+        hipLaunchKernelGGL((prefill_kernel<false, true>), dim3((unsigned)blocks), dim3(PF_THREADS), 0, stream, p);
+    else if (P > 0)
+        hipLaunchKernelGGL((prefill_kernel<true, false>), dim3((unsigned)blocks), dim3(PF_THREADS), 0, stream, p);
     else
-        hipLaunchKernelGGL(prefill_kernel<false>, dim3((unsigned)blocks), dim3(PF_THREADS), 0, stream, p);
+        hipLaunchKernelGGL((prefill_kernel<false, false>), dim3((unsigned)blocks), dim3(PF_THREADS), 0, stream, p);
     return hipGetLastError();
 }
 

@@ -252,6 +252,43 @@ int gdla_prep(void *q_signal, void *q_noise, const void *k_rope, void *k, const 
               int B, int T, int n_kv, int group, int d_qk, int d_v, int d_model, int pos0,
               float rope_theta, void *stream);
 
+/*
+ * gdla_prefill_backward_workspace_size -- bytes of device workspace
+ * gdla_prefill_backward needs (0 for invalid arguments).
+ */
+size_t gdla_prefill_backward_workspace_size(int B, int T, int n_kv);
+
+/*
+ * gdla_prefill_backward -- gradients of gdla_prefill (P = 0) with respect to
+ * its six inputs, given d_out, the gradient of a loss with respect to out.
+ * The derivatives of the attention core (aitrends.kr, GDLA paragraphs: per KV
+ * head j, signal heads 4j..4j+3 and noise head j attend with K_j, V_j;
+ * D = H_S - lambda (.) Repeat_4(H_N); out = gate (.) D):
+ *     dgate = d_out (.) D,  dD = gate (.) d_out,
+ *     dlambda_h = -sum_d dD_h H_N,   dH_S = dD,   dH_N,j = -sum_{h in j} lambda_h dD_h,
+ * then per head, with P its softmax weights and delta = rowsum(dH (.) H):
+ *     dV_j += P^T dH,  dS = P (.) (dH V_j^T - delta),  dQ = scale dS K_j,
+ *     dK_j += scale dS^T Q.
+ * The call recomputes the forward first (the pages' long-context training
+ * recomputes activations operator by operator), so it needs only the forward's
+ * inputs.  Arguments as for gdla_prefill; the outputs
+ *   dq_signal [B, T, n_kv*group, d_qk], dq_noise [B, T, n_kv, d_qk],
+ *   dk [B, T, n_kv, d_qk], dv [B, T, n_kv, d_v], dlambda [B, T, n_kv*group],
+ *   dgate [B, T, n_kv*group, d_v]
+ * are bf16, every element written; none may overlap an input, another output
+ * or the workspace.  workspace: device scratch of at least
+ * gdla_prefill_backward_workspace_size(B, T, n_kv) bytes, 256-byte aligned,
+ * contents ignored; calls sharing one must be ordered on one stream.
+ * Products are bf16 with fp32 accumulation; P and dS are rounded to bf16
+ * before the products that take them.  B = 0 or T = 0 is a valid empty call;
+ * B and n_kv must be <= 65535.  Shape support as for gdla_prefill.
+ */
+int gdla_prefill_backward(const void *q_signal, const void *q_noise, const void *k, const void *v,
+                          const void *lambda_, const void *gate, const void *d_out, void *dq_signal,
+                          void *dq_noise, void *dk, void *dv, void *dlambda, void *dgate,
+                          void *workspace, size_t workspace_bytes, int B, int T, int n_kv, int group,
+                          int d_qk, int d_v, int window, float softmax_scale, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -239,3 +239,48 @@ def test_prep_rejections(lib):
 def test_prep_empty_is_noop(lib):
     assert prep(lib, [None] * 9, B=0) == OK
     assert prep(lib, [None] * 9, T=0) == OK
+
+
+def backward(lib, ptrs=None, ws=A + 0x40000000000, ws_bytes=1 << 40, B=1, T=64, n_kv=16, group=4, d_qk=192,
+             d_v=128, window=0, scale=0.07):
+    if ptrs is None:
+        ptrs = [A + i * (1 << 36) for i in range(13)]
+    return lib.gdla_prefill_backward(*ptrs, ws, ws_bytes, B, T, n_kv, group, d_qk, d_v, window,
+                                     ctypes.c_float(scale), None)
+
+
+def test_backward_workspace_size(lib):
+    one = lib.gdla_prefill_backward_workspace_size(1, 64, 16)
+    assert one > 0 and one % 256 == 0
+    assert lib.gdla_prefill_backward_workspace_size(2, 64, 16) > one
+    assert lib.gdla_prefill_backward_workspace_size(-1, 64, 16) == 0
+
+
+def test_backward_rejections(lib):
+    assert backward(lib, B=-1) == INVALID
+    assert backward(lib, group=2) == UNSUPPORTED
+    assert backward(lib, window=-1) == INVALID
+    assert backward(lib, scale=0.0) == INVALID
+    assert backward(lib, B=70000) == INVALID
+    for i in range(13):
+        ptrs = [A + k * (1 << 36) for k in range(13)]
+        ptrs[i] = None
+        assert backward(lib, ptrs) == INVALID
+        ptrs[i] = A + 8 + i * (1 << 36)
+        assert backward(lib, ptrs) == MISALIGNED
+    need = lib.gdla_prefill_backward_workspace_size(1, 64, 16)
+    assert backward(lib, ws=None) == WORKSPACE
+    assert backward(lib, ws_bytes=need - 1) == WORKSPACE
+    assert backward(lib, ws=A + 0x40000000000 + 64) == MISALIGNED
+    # dk inside k
+    ptrs = [A + k * (1 << 36) for k in range(13)]
+    ptrs[9] = ptrs[2] + 1024
+    assert backward(lib, ptrs) == INVALID
+    assert b"overlaps" in lib.gdla_last_error()
+    # workspace inside dv
+    assert backward(lib, ws=A + 10 * (1 << 36)) == INVALID
+
+
+def test_backward_empty_is_noop(lib):
+    assert backward(lib, [None] * 13, ws=None, ws_bytes=0, B=0) == OK
+    assert backward(lib, [None] * 13, ws=None, ws_bytes=0, T=0) == OK

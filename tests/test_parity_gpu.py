@@ -461,3 +461,83 @@ def test_prep_config_4k():
     check_prep(gpu_prep(d, 0), d, 0)
     del d
     torch.cuda.empty_cache()
+
+
+# ----------------------------------------------------------------------------
+# gradients of the prefill
+# ----------------------------------------------------------------------------
+
+def compare_grad(got, want, what):
+    """rel-L2 <= 1e-2, and no element off by more than 3e-2 of the tensor's
+    largest magnitude (at least 1): the gradients pass through bf16 weights and
+    bf16 dS (2^-9 relative each) and are stored in bf16."""
+    g = got.detach().double().cpu().numpy()
+    w = want.detach().double().cpu().numpy() if isinstance(want, torch.Tensor) else np.asarray(want, np.float64)
+    assert g.shape == w.shape, (what, g.shape, w.shape)
+    assert np.isfinite(g).all(), "%s: non-finite values" % what
+    nw = np.linalg.norm(w)
+    rel = np.linalg.norm(g - w) / nw if nw > 0 else np.linalg.norm(g - w)
+    mabs = float(np.abs(g - w).max()) if g.size else 0.0
+    ref = max(1.0, float(np.abs(w).max()) if w.size else 0.0)
+    log("%s: rel_l2=%.3e max_abs=%.3e (largest |want| %.3e)" % (what, rel, mabs, ref))
+    assert rel <= 1e-2, "%s: rel_l2 %.3e" % (what, rel)
+    assert mabs <= 3e-2 * ref, "%s: max_abs %.3e > 3e-2 * %.3e" % (what, mabs, ref)
+
+
+def backward_case(B, T, n_kv, window, q_std, seed):
+    import attention_gdla_prefill_amd as gdla
+    from oracle import backward as ob
+    w = W.Workload("bwd", "prefill", B=B, T=T, n_kv=n_kv, window=window)
+    x = to_dev(W.prefill_inputs(w, seed=seed, q_std=q_std))
+    gen = torch.Generator().manual_seed(seed + 1)
+    d_out = torch.randn((B, T, 4 * n_kv, 128), generator=gen).to(torch.bfloat16).cuda()
+    got = gdla.prefill_backward(x["q_signal"], x["q_noise"], x["k"], x["v"], x["lam"], x["gate"], d_out,
+                                window=window)
+    torch.cuda.synchronize()
+    want = ob.backward(*[x[n] for n in ("q_signal", "q_noise", "k", "v", "lam", "gate")], d_out, window=window)
+    for name, key in (("q_signal", "q_signal"), ("q_noise", "q_noise"), ("k", "k"), ("v", "v"), ("lam", "lam"),
+                      ("gate", "gate")):
+        compare_grad(got[name], want[key], "d%s B%d T%d kv%d W%d" % (name, B, T, n_kv, window))
+
+
+BACKWARD_CASES = [
+    # (B, T, n_kv, window, q_std): several tiles and a ragged tail; windows of
+    # 1, a few keys, one tile, two tiles; sharper scores (q_std 1)
+    (1, 70, 2, 0, None), (1, 70, 2, 5, None), (2, 130, 1, 64, None), (1, 1, 1, 0, None),
+    (1, 200, 3, 128, 1.0), (1, 97, 2, 1, None), (1, 150, 1, 0, 1.0),
+]
+
+
+@pytest.mark.parametrize("case", BACKWARD_CASES, ids=lambda c: "B%d_T%d_kv%d_W%d_q%s" % c)
+def test_backward_matches_oracle(case):
+    B, T, n_kv, window, q_std = case
+    log("backward B=%d T=%d n_kv=%d W=%d" % (B, T, n_kv, window))
+    backward_case(B, T, n_kv, window, q_std, seed=100 + T)
+
+
+def test_backward_config_4k_one_kv_head():
+    """The full 4K prefill (16 KV heads); the gradients of KV head 5's group
+    checked in full against the oracle run on that group alone (its gradients
+    depend on its own heads only)."""
+    import attention_gdla_prefill_amd as gdla
+    from oracle import backward as ob
+    w = W.WORKLOADS["pf_full_4k"]
+    log("backward at pf_full_4k, KV head 5 checked")
+    x = W.prefill_inputs(w, seed=0, device="cuda")
+    gen = torch.Generator().manual_seed(1)
+    d_out = torch.randn((1, w.T, w.n_sig, 128), generator=gen).to(torch.bfloat16).cuda()
+    got = gdla.prefill_backward(x["q_signal"], x["q_noise"], x["k"], x["v"], x["lam"], x["gate"], d_out)
+    torch.cuda.synchronize()
+    j = 5
+    sig = slice(4 * j, 4 * j + 4)
+    sl = dict(q_signal=x["q_signal"][:, :, sig], q_noise=x["q_noise"][:, :, j:j + 1], k=x["k"][:, :, j:j + 1],
+              v=x["v"][:, :, j:j + 1], lam=x["lam"][:, :, sig], gate=x["gate"][:, :, sig])
+    want = ob.backward(*[sl[n] for n in ("q_signal", "q_noise", "k", "v", "lam", "gate")], d_out[:, :, sig])
+    compare_grad(got["q_signal"][:, :, sig], want["q_signal"], "dq_signal 4k head group 5")
+    compare_grad(got["q_noise"][:, :, j:j + 1], want["q_noise"], "dq_noise 4k head group 5")
+    compare_grad(got["k"][:, :, j:j + 1], want["k"], "dk 4k head 5")
+    compare_grad(got["v"][:, :, j:j + 1], want["v"], "dv 4k head 5")
+    compare_grad(got["lam"][:, :, sig], want["lam"], "dlambda 4k head group 5")
+    compare_grad(got["gate"][:, :, sig], want["gate"], "dgate 4k head group 5")
+    del x, got
+    torch.cuda.empty_cache()
