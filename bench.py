@@ -65,11 +65,61 @@ def decode_latent_bytes(lengths, window, n_kv=16, n_sig=64):
     return sum(vis) * 576 * 2 + len(lengths) * per_seq + weights + 4 * (len(lengths) + 1)
 
 
+PREFILL_SOURCES = ("prefill_gfx950.hip", "gdla_device.h")
+
+
 def source_hash():
+    """Hash of the files the prefill kernel is built from (its traffic figures
+    hold while these are unchanged)."""
     h = hashlib.sha256()
-    for p in sorted(glob.glob(os.path.join(ROOT, "attention_gdla_prefill_amd", "csrc", "*"))):
-        h.update(open(p, "rb").read())
+    for name in PREFILL_SOURCES:
+        h.update(open(os.path.join(ROOT, "attention_gdla_prefill_amd", "csrc", name), "rb").read())
     return h.hexdigest()[:16]
+
+
+def _counter_rows(run_dir, counter):
+    """(kernel name, value) per dispatch from a rocprofv3 --pmc csv run."""
+    import csv
+    paths = glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True)
+    if not paths:
+        raise SystemExit("no counter_collection.csv under %s" % run_dir)
+    rows = []
+    with open(paths[0]) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] == counter:
+                rows.append((r["Kernel_Name"], float(r["Counter_Value"])))
+    return rows
+
+
+def record_traffic(workload, fetch_dir, write_dir):
+    """Writes profiles/traffic_<workload>.json from two counter runs of
+    `bench.py --workload <workload> --steps 5 --warmup 2 --no-cpu-baseline
+    --no-extra --copy-probe` (FETCH_SIZE, then WRITE_SIZE): the prefill
+    kernel's median per dispatch, each counter scaled by what it reads for the
+    1 GiB device copy that ends the run."""
+    import statistics
+    out = {"kernel": "prefill_kernel", "workload": workload, "source_hash": source_hash()}
+    scaled = {}
+    for key, run_dir, counter in (("fetch", fetch_dir, "FETCH_SIZE"), ("write", write_dir, "WRITE_SIZE")):
+        rows = _counter_rows(run_dir, counter)
+        kern = [v for n, v in rows if "prefill_kernel" in n]
+        copy = [v for n, v in rows if "copy" in n.lower()]
+        if not kern or not copy:
+            raise SystemExit("%s: prefill or copy dispatches missing" % run_dir)
+        per = statistics.median(kern)
+        probe = copy[-1]
+        scale = (1 << 30) / 1024.0 / probe
+        out["%s_kib_per_dispatch" % key] = per
+        out["%s_scale" % key] = scale
+        out["copy_probe_%s_kib" % key] = probe
+        scaled[key] = per * 1024.0 * scale
+    out["read_bytes"] = scaled["fetch"]
+    out["written_bytes"] = scaled["write"]
+    out["bytes_per_launch"] = scaled["fetch"] + scaled["write"]
+    path = os.path.join(ROOT, "profiles", "traffic_%s.json" % workload)
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out))
 
 
 def time_kernel(fn, steps, warmup, stream):
@@ -205,6 +255,34 @@ def bench_prep(name, steps, warmup):
             "cache": "cold (512 MB buffer rewritten before each launch)"}
 
 
+def bench_backward(name, steps, warmup):
+    """The prefill backward (forward recomputed inside) at prefill workload
+    name, warm.  Algorithmic FLOPs: 1664 per unmasked (head, query, key) pair
+    -- the scores again (2*192), dP = dH V^T (2*128), dV (2*128), dK (2*192),
+    dQ (2*192); the kernels issue 2944 (the saving forward's 640, and the
+    scores and dP once in each of the two gradient kernels)."""
+    import torch
+    import attention_gdla_prefill_amd as gdla
+    import workload as W
+    w = W.WORKLOADS[name]
+    x = W.prefill_inputs(w, seed=0, device="cuda")
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(1)
+    d_out = torch.randn((w.B, w.T, w.n_sig, w.d_v), generator=gen, device="cuda").to(torch.bfloat16)
+    ws = torch.empty(gdla.prefill_backward_workspace_size(w.B, w.T, w.n_kv), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    fn = lambda: gdla.prefill_backward(x["q_signal"], x["q_noise"], x["k"], x["v"], x["lam"], x["gate"], d_out,
+                                       window=w.window, workspace=ws)
+    wall, ev = time_kernel(fn, steps, warmup, stream)
+    ms = sum(ev) / len(ev)
+    pairs = pairs_prefill(w.B, w.T, w.window, 0) * (w.n_sig + w.n_kv)
+    del x, d_out, ws
+    torch.cuda.empty_cache()
+    return {"ms": ms, "tflops": pairs * 1664 / (ms * 1e-3) / 1e12,
+            "mfma_frac": pairs * 1664 / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+            "issued_tflops": pairs * 2944 / (ms * 1e-3) / 1e12, "steps": steps}
+
+
 def bench_decode(name, steps, warmup):
     import torch
     import attention_gdla_prefill_amd as gdla
@@ -330,7 +408,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--extras", default="pf_swa_32k,pf_full_128k,pf_prefix_4k_32k,pf_swa_rank,"
-                                        "dec_full,dec_swa,dec_latent_full,dec_latent_swa,prep_4k,prep_swa_32k",
+                                        "dec_full,dec_swa,dec_latent_full,dec_latent_swa,prep_4k,prep_swa_32k,bwd_4k",
                     help="comma-separated extra workloads to time (a profile of one workload "
                          "names just that one)")
     ap.add_argument("--copy-probe", action="store_true",
@@ -338,7 +416,13 @@ def main():
     ap.add_argument("--peaks", action="store_true",
                     help="also time a bf16 8192^3 GEMM (hipBLASLt via torch) and a 1 GiB device "
                          "copy: achievable-rate references, reported under 'peaks'")
+    ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write profiles/traffic_<workload>.json from two rocprofv3 --pmc runs "
+                         "(FETCH_SIZE, WRITE_SIZE) of this script with --copy-probe, then exit")
     args = ap.parse_args()
+    if args.record_traffic:
+        record_traffic(args.workload, *args.record_traffic)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)",
               file=sys.stderr)
@@ -346,7 +430,7 @@ def main():
     wanted = [] if args.no_extra else [x for x in args.extras.split(",") if x]
     for name in wanted:
         if name not in ("pf_swa_32k", "pf_full_128k", "pf_prefix_4k_32k", "pf_swa_rank", "dec_full",
-                        "dec_swa", "dec_latent_full", "dec_latent_swa", "prep_4k", "prep_swa_32k"):
+                        "dec_swa", "dec_latent_full", "dec_latent_swa", "prep_4k", "prep_swa_32k", "bwd_4k"):
             print("unknown extra workload %r" % name, file=sys.stderr)
             sys.exit(2)
 
@@ -392,6 +476,9 @@ def main():
                 continue
             print("[bench] extra %s" % name, file=sys.stderr, flush=True)
             extra[name] = dict(bench_prep(shape, 20, 5), shapes=shape)
+        if "bwd_4k" in wanted:
+            print("[bench] extra bwd_4k", file=sys.stderr, flush=True)
+            extra["bwd_4k"] = dict(bench_backward("pf_full_4k", 20, 10), shapes="pf_full_4k")
 
     peaks = measured_peaks() if args.peaks else None
 
