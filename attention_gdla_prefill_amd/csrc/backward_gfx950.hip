@@ -30,8 +30,11 @@ namespace gdla {
 
 constexpr int BW_T = 64;                   // query tile and key block
 constexpr int BW_THREADS = 256;
-constexpr int BW_QROW = D_QK + 8;          // LDS row of a Q or K tile (bf16), padded
-constexpr int BW_VROW = D_V + 8;           // LDS row of a dH or V tile (bf16), padded
+// LDS rows padded by 32 bytes: the 16 rows a fragment read or a transposing
+// read touches then fall in distinct banks (a 16-byte pad leaves ~40 % of the
+// LDS cycles in bank conflicts)
+constexpr int BW_QROW = D_QK + 16;         // LDS row of a Q or K tile (bf16)
+constexpr int BW_VROW = D_V + 16;          // LDS row of a dH or V tile (bf16)
 
 struct BwdParams {
     const __bf16 *qs, *qn, *k, *v, *lam, *gate, *dout;
@@ -60,18 +63,44 @@ __device__ __forceinline__ bf16x8 bw_tr_a(const __bf16 *m, int rs, int row0, int
     return __builtin_bit_cast(bf16x8, v8);
 }
 
-// cooperative copy of n_rows rows of `cols` bf16 (a multiple of 8) from global
-// (row stride gs) into LDS (row stride ls); rows past n_valid are zero
-__device__ __forceinline__ void bw_load_tile(__bf16 *lds, int ls, const __bf16 *src, long gs, int n_valid,
-                                             int cols) {
-    const int cpr = cols / 8;
-    for (int i = threadIdx.x; i < BW_T * cpr; i += BW_THREADS) {
-        const int row = i / cpr, c = (i % cpr) * 8;
-        u32x4 w = {0, 0, 0, 0};
-        if (row < n_valid) w = ldg16(src + row * gs + c);
-        *reinterpret_cast<u32x4 *>(lds + row * ls + c) = w;
+
+// A 64-row tile pair staged through registers: the global loads of the next
+// step are issued before the current step computes and land in the other LDS
+// buffer after it, so the copy runs under the products.  Thread t holds
+// chunks t, t+256, .. of the first tile (cols_a values per row) and of the
+// second (cols_b), 16 bytes each.
+template <int COLS_A, int COLS_B>
+struct BwStage {
+    static constexpr int NA = BW_T * COLS_A / 8 / BW_THREADS, NB = BW_T * COLS_B / 8 / BW_THREADS;
+    u32x4 a[NA], b[NB];
+    float x0, x1;                          // two per-row scalars (threads < 64)
+    __device__ __forceinline__ void load(const __bf16 *sa, long gsa, const __bf16 *sb, long gsb, int n_valid) {
+        const u32x4 z = {0, 0, 0, 0};
+#pragma unroll
+        for (int i = 0; i < NA; ++i) {
+            const int c = threadIdx.x + BW_THREADS * i, row = c / (COLS_A / 8), col = (c % (COLS_A / 8)) * 8;
+            a[i] = row < n_valid ? ldg16(sa + row * gsa + col) : z;
+        }
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+            const int c = threadIdx.x + BW_THREADS * i, row = c / (COLS_B / 8), col = (c % (COLS_B / 8)) * 8;
+            b[i] = row < n_valid ? ldg16(sb + row * gsb + col) : z;
+        }
     }
-}
+    __device__ __forceinline__ void store(__bf16 *la, int lsa, __bf16 *lb, int lsb) const {
+#pragma unroll
+        for (int i = 0; i < NA; ++i) {
+            const int c = threadIdx.x + BW_THREADS * i, row = c / (COLS_A / 8), col = (c % (COLS_A / 8)) * 8;
+            *reinterpret_cast<u32x4 *>(la + row * lsa + col) = a[i];
+        }
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+            const int c = threadIdx.x + BW_THREADS * i, row = c / (COLS_B / 8), col = (c % (COLS_B / 8)) * 8;
+            *reinterpret_cast<u32x4 *>(lb + row * lsb + col) = b[i];
+        }
+    }
+};
+static_assert(BW_T * D_QK / 8 % BW_THREADS == 0 && BW_T * D_V / 8 % BW_THREADS == 0, "tile chunks per thread");
 
 __device__ __forceinline__ bool bw_visible(int q, int key, int T, int window) {
     return q < T && key <= q && (window == 0 || q - key < window);
@@ -162,14 +191,18 @@ __device__ __forceinline__ BwHead bw_head(const BwdParams &p, int b, int j, int 
     return x;
 }
 
-// ---- 2. dK, dV.  Workgroup (64-key block, KV head j, sequence b); wave w owns
-// keys kb0 + 16w .. +15.  In C layout lane (r, g) holds element
-// [query 16qb + 4g + e][key r] of S, P, dP, dS.
-__global__ __launch_bounds__(BW_THREADS) void bwd_dkdv_kernel(BwdParams p) {
-    __shared__ __attribute__((aligned(16))) __bf16 Qs[BW_T * BW_QROW];
-    __shared__ __attribute__((aligned(16))) __bf16 Hs[BW_T * BW_VROW];
-    __shared__ float lse_s[BW_T], dl_s[BW_T];
-    const int kb0 = blockIdx.x * BW_T, j = blockIdx.y, b = blockIdx.z;
+// ---- 2. dK, dV.  Workgroup (KV head j, 64-key block, sequence b); wave w owns
+// keys kb0 + 16w .. +15.  Steps: (query tile, head) for every query tile that
+// sees a key of the block and each of the 5 heads; the Q and dH tiles of the
+// next step are copied while the current one computes (two LDS buffers).  In C
+// layout lane (r, g) holds element [query 16qb + 4g + e][key r] of S, P, dP, dS.
+__global__ __launch_bounds__(BW_THREADS, 1) void bwd_dkdv_kernel(BwdParams p) {
+    __shared__ __attribute__((aligned(16))) __bf16 Qs[2][BW_T * BW_QROW];
+    __shared__ __attribute__((aligned(16))) __bf16 Hs[2][BW_T * BW_VROW];
+    __shared__ __attribute__((aligned(16))) float lse_s[2][BW_T], dl_s[2][BW_T];
+    // the KV head is the fastest grid index, so the workgroups are dispatched
+    // longest first (key block 0 sees every query tile)
+    const int j = blockIdx.x, kb0 = blockIdx.y * BW_T, b = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, r = lane & 15, g = lane >> 4;
     const int n_h = p.n_kv * HEADS, T = p.T;
     const int key = kb0 + 16 * wave + r;
@@ -196,64 +229,90 @@ __global__ __launch_bounds__(BW_THREADS) void bwd_dkdv_kernel(BwdParams p) {
     const int qt_lo = kb0 / BW_T;
     int qt_hi = (T - 1) / BW_T;
     if (p.window > 0) qt_hi = min(qt_hi, (kb0 + BW_T - 1 + p.window - 1) / BW_T);
-    for (int qt = qt_lo; qt <= qt_hi; ++qt) {
-        const int q0 = qt * BW_T, n_valid = min(BW_T, T - q0);
-        for (int h = 0; h < HEADS; ++h) {
-            const BwHead hd = bw_head(p, b, j, h);
-            __syncthreads();                          // the previous tile is consumed
-            bw_load_tile(Qs, BW_QROW, hd.q + (long)q0 * hd.q_stride, hd.q_stride, n_valid, D_QK);
-            bw_load_tile(Hs, BW_VROW, hd.dh + (long)q0 * hd.dh_stride, hd.dh_stride, n_valid, D_V);
-            if (tid < BW_T) {
-                const long row = (long)b * T + q0 + tid;
-                lse_s[tid] = tid < n_valid ? p.lse[row * n_h + hd.col] : 0.f;
-                dl_s[tid] = tid < n_valid ? p.delta[row * n_h + hd.col] : 0.f;
-            }
-            __syncthreads();
-            // S = Q K_w^T and dP = dH V_w^T, four 16-query blocks
-            f32x4 s[4], dp[4];
-#pragma unroll
-            for (int qb = 0; qb < 4; ++qb) {
-                const __bf16 *qa = Qs + (16 * qb + r) * BW_QROW + 8 * g;
-                const __bf16 *ha = Hs + (16 * qb + r) * BW_VROW + 8 * g;
-                s[qb] = zero4;
-                dp[qb] = zero4;
-#pragma unroll
-                for (int kk = 0; kk < D_QK / 32; ++kk)
-                    s[qb] = mfma16(*reinterpret_cast<const bf16x8 *>(qa + 32 * kk), kf[kk], s[qb]);
-#pragma unroll
-                for (int kk = 0; kk < D_V / 32; ++kk)
-                    dp[qb] = mfma16(*reinterpret_cast<const bf16x8 *>(ha + 32 * kk), vf[kk], dp[qb]);
-            }
-            // P and dS; packed as B operands over query pairs (blocks 2i, 2i+1)
-            uint32_t pw[4][2], sw[4][2];
-#pragma unroll
-            for (int qb = 0; qb < 4; ++qb) {
-                float pv[4], dsv[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int ql = 16 * qb + 4 * g + e;
-                    const bool vis = bw_visible(q0 + ql, key, T, p.window) && key < T;
-                    pv[e] = vis ? fast_exp2(fmaf(s[qb][e], p.scale_log2, -lse_s[ql])) : 0.f;
-                    dsv[e] = pv[e] * (dp[qb][e] - dl_s[ql]);
-                }
-                pw[qb][0] = pack_bf16x2(pv[0], pv[1]);
-                pw[qb][1] = pack_bf16x2(pv[2], pv[3]);
-                sw[qb][0] = pack_bf16x2(dsv[0], dsv[1]);
-                sw[qb][1] = pack_bf16x2(dsv[2], dsv[3]);
-            }
-#pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const bf16x8 pb = __builtin_bit_cast(bf16x8, (u32x4{pw[2 * i][0], pw[2 * i][1], pw[2 * i + 1][0],
-                                                                    pw[2 * i + 1][1]}));
-                const bf16x8 sb = __builtin_bit_cast(bf16x8, (u32x4{sw[2 * i][0], sw[2 * i][1], sw[2 * i + 1][0],
-                                                                    sw[2 * i + 1][1]}));
-                // dV^T += dH^T P, dK^T += Q^T dS over the 32 queries of pair i
-#pragma unroll
-                for (int db = 0; db < D_V / 16; ++db) dv[db] = mfma16(bw_tr_a(Hs, BW_VROW, 32 * i, 16 * db, r, g), pb, dv[db]);
-#pragma unroll
-                for (int db = 0; db < D_QK / 16; ++db) dk[db] = mfma16(bw_tr_a(Qs, BW_QROW, 32 * i, 16 * db, r, g), sb, dk[db]);
-            }
+    const int n_steps = (qt_hi - qt_lo + 1) * HEADS;
+    BwStage<D_QK, D_V> st;
+    auto fetch = [&](int it) {
+        const int q0 = (qt_lo + it / HEADS) * BW_T, n_valid = min(BW_T, T - q0);
+        const BwHead hd = bw_head(p, b, j, it % HEADS);
+        st.load(hd.q + (long)q0 * hd.q_stride, hd.q_stride, hd.dh + (long)q0 * hd.dh_stride, hd.dh_stride, n_valid);
+        if (tid < BW_T) {
+            const long row = (long)b * T + q0 + tid;
+            st.x0 = tid < n_valid ? p.lse[row * n_h + hd.col] : 0.f;
+            st.x1 = tid < n_valid ? p.delta[row * n_h + hd.col] : 0.f;
         }
+    };
+    auto stage = [&](int buf) {
+        st.store(Qs[buf], BW_QROW, Hs[buf], BW_VROW);
+        if (tid < BW_T) {
+            lse_s[buf][tid] = st.x0;
+            dl_s[buf][tid] = st.x1;
+        }
+    };
+    fetch(0);
+    stage(0);
+    __syncthreads();
+    for (int it = 0; it < n_steps; ++it) {
+        const int buf = it & 1, q0 = (qt_lo + it / HEADS) * BW_T;
+        if (it + 1 < n_steps) fetch(it + 1);
+        const __bf16 *qs_ = Qs[buf], *hs_ = Hs[buf];
+        // S = Q K_w^T and dP = dH V_w^T, four 16-query blocks
+        f32x4 s[4], dp[4];
+#pragma unroll
+        for (int qb = 0; qb < 4; ++qb) {
+            const __bf16 *qa = qs_ + (16 * qb + r) * BW_QROW + 8 * g;
+            const __bf16 *ha = hs_ + (16 * qb + r) * BW_VROW + 8 * g;
+            s[qb] = zero4;
+            dp[qb] = zero4;
+#pragma unroll
+            for (int kk = 0; kk < D_QK / 32; ++kk)
+                s[qb] = mfma16(*reinterpret_cast<const bf16x8 *>(qa + 32 * kk), kf[kk], s[qb]);
+#pragma unroll
+            for (int kk = 0; kk < D_V / 32; ++kk)
+                dp[qb] = mfma16(*reinterpret_cast<const bf16x8 *>(ha + 32 * kk), vf[kk], dp[qb]);
+        }
+        // P and dS; packed as B operands over query pairs (blocks 2i, 2i+1).
+        // The rows' log2-sum-exp and delta are read first and the weight is
+        // computed for every element, then selected (no branch per element).
+        float4 lse4[4], dl4[4];
+#pragma unroll
+        for (int qb = 0; qb < 4; ++qb) {
+            lse4[qb] = *reinterpret_cast<const float4 *>(&lse_s[buf][16 * qb + 4 * g]);
+            dl4[qb] = *reinterpret_cast<const float4 *>(&dl_s[buf][16 * qb + 4 * g]);
+        }
+        uint32_t pw[4][2], sw[4][2];
+#pragma unroll
+        for (int qb = 0; qb < 4; ++qb) {
+            const float ls[4] = {lse4[qb].x, lse4[qb].y, lse4[qb].z, lse4[qb].w};
+            const float dls[4] = {dl4[qb].x, dl4[qb].y, dl4[qb].z, dl4[qb].w};
+            float pv[4], dsv[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int ql = 16 * qb + 4 * g + e;
+                const float x = fast_exp2(fmaf(s[qb][e], p.scale_log2, -ls[e]));
+                pv[e] = bw_visible(q0 + ql, key, T, p.window) ? x : 0.f;
+                dsv[e] = pv[e] * (dp[qb][e] - dls[e]);
+            }
+            pw[qb][0] = pack_bf16x2(pv[0], pv[1]);
+            pw[qb][1] = pack_bf16x2(pv[2], pv[3]);
+            sw[qb][0] = pack_bf16x2(dsv[0], dsv[1]);
+            sw[qb][1] = pack_bf16x2(dsv[2], dsv[3]);
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const bf16x8 pb = __builtin_bit_cast(bf16x8, (u32x4{pw[2 * i][0], pw[2 * i][1], pw[2 * i + 1][0],
+                                                                pw[2 * i + 1][1]}));
+            const bf16x8 sb = __builtin_bit_cast(bf16x8, (u32x4{sw[2 * i][0], sw[2 * i][1], sw[2 * i + 1][0],
+                                                                sw[2 * i + 1][1]}));
+            // dV^T += dH^T P, dK^T += Q^T dS over the 32 queries of pair i
+#pragma unroll
+            for (int db = 0; db < D_V / 16; ++db) dv[db] = mfma16(bw_tr_a(hs_, BW_VROW, 32 * i, 16 * db, r, g), pb, dv[db]);
+#pragma unroll
+            for (int db = 0; db < D_QK / 16; ++db) dk[db] = mfma16(bw_tr_a(qs_, BW_QROW, 32 * i, 16 * db, r, g), sb, dk[db]);
+        }
+        // the next step's tiles into the other buffer (its last reader was step
+        // it-1, which every wave finished before the previous barrier)
+        if (it + 1 < n_steps) stage(buf ^ 1);
+        __syncthreads();
     }
     // lane (r, g) holds dV[key r][16db + 4g + e] and dK[key r][16db + 4g + e] / scale
     if (key < T) {
@@ -269,13 +328,16 @@ __global__ __launch_bounds__(BW_THREADS) void bwd_dkdv_kernel(BwdParams p) {
     }
 }
 
-// ---- 3. dQ.  Workgroup (64-query tile, KV head j, sequence b); wave w owns
-// queries q0 + 16w .. +15.  In C layout lane (r, g) holds element
+// ---- 3. dQ.  Workgroup (KV head j, 64-query tile, sequence b); wave w owns
+// queries q0 + 16w .. +15.  Steps: (head, key block) over the 5 heads and the
+// key blocks the tile sees; the K and V tiles of the next step are copied while
+// the current one computes.  In C layout lane (r, g) holds element
 // [key 16kb + 4g + e][query r] of S^T, P^T, dP^T, dS^T.
-__global__ __launch_bounds__(BW_THREADS) void bwd_dq_kernel(BwdParams p) {
-    __shared__ __attribute__((aligned(16))) __bf16 Ks[BW_T * BW_QROW];
-    __shared__ __attribute__((aligned(16))) __bf16 Vs[BW_T * BW_VROW];
-    const int q0 = blockIdx.x * BW_T, j = blockIdx.y, b = blockIdx.z;
+__global__ __launch_bounds__(BW_THREADS, 1) void bwd_dq_kernel(BwdParams p) {
+    __shared__ __attribute__((aligned(16))) __bf16 Ks[2][BW_T * BW_QROW];
+    __shared__ __attribute__((aligned(16))) __bf16 Vs[2][BW_T * BW_VROW];
+    // longest first: the last query tiles see the most key blocks
+    const int j = blockIdx.x, q0 = (gridDim.y - 1 - blockIdx.y) * BW_T, b = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, r = lane & 15, g = lane >> 4;
     const int n_h = p.n_kv * HEADS, T = p.T;
     const int q = q0 + 16 * wave + r;
@@ -283,15 +345,28 @@ __global__ __launch_bounds__(BW_THREADS) void bwd_dq_kernel(BwdParams p) {
     const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
     const int kb_lo = p.window > 0 ? max(0, q0 - p.window + 1) / BW_T : 0;
     const int kb_hi = (min(q0 + BW_T, T) - 1) / BW_T;
+    const int n_kb = kb_hi - kb_lo + 1, n_steps = HEADS * n_kb;
     const __bf16 *kseq = p.k + ((long)b * T * p.n_kv + j) * D_QK;
     const __bf16 *vseq = p.v + ((long)b * T * p.n_kv + j) * D_V;
     const long kv_qs = (long)p.n_kv * D_QK, kv_vs = (long)p.n_kv * D_V;
+    BwStage<D_QK, D_V> st;
+    auto fetch = [&](int it) {
+        const int k0 = (kb_lo + it % n_kb) * BW_T;
+        st.load(kseq + (long)k0 * kv_qs, kv_qs, vseq + (long)k0 * kv_vs, kv_vs, min(BW_T, T - k0));
+    };
+    fetch(0);
+    st.store(Ks[0], BW_QROW, Vs[0], BW_VROW);
+    __syncthreads();
 
-    for (int h = 0; h < HEADS; ++h) {
+    bf16x8 qf[D_QK / 32], hf[D_V / 32];
+    float lse = 0.f, dl = 0.f;
+    f32x4 dq[D_QK / 16];
+    for (int it = 0; it < n_steps; ++it) {
+        const int h = it / n_kb, buf = it & 1, k0 = (kb_lo + it % n_kb) * BW_T;
         const BwHead hd = bw_head(p, b, j, h);
-        // B operands Q_w^T and dH_w^T (lane: row q, values 32kk + 8g ..)
-        bf16x8 qf[D_QK / 32], hf[D_V / 32];
-        {
+        if (it % n_kb == 0) {
+            // a new head: its B operands Q_w^T and dH_w^T (lane: row q, values
+            // 32kk + 8g ..), requested before the next step's copy
             const u32x4 z = {0, 0, 0, 0};
             const long qi = q_ok ? q : 0;
 #pragma unroll
@@ -300,53 +375,47 @@ __global__ __launch_bounds__(BW_THREADS) void bwd_dq_kernel(BwdParams p) {
 #pragma unroll
             for (int kk = 0; kk < D_V / 32; ++kk)
                 hf[kk] = __builtin_bit_cast(bf16x8, q_ok ? ldg16(hd.dh + qi * hd.dh_stride + 32 * kk + 8 * g) : z);
+            const long row = (long)b * T + qi;
+            lse = q_ok ? p.lse[row * n_h + hd.col] : 0.f;
+            dl = q_ok ? p.delta[row * n_h + hd.col] : 0.f;
+#pragma unroll
+            for (int i = 0; i < D_QK / 16; ++i) dq[i] = zero4;
         }
-        const long row = (long)b * T + (q_ok ? q : 0);
-        const float lse = q_ok ? p.lse[row * n_h + hd.col] : 0.f;
-        const float dl = q_ok ? p.delta[row * n_h + hd.col] : 0.f;
-        f32x4 dq[D_QK / 16];
+        if (it + 1 < n_steps) fetch(it + 1);
+        const __bf16 *ks_ = Ks[buf], *vs_ = Vs[buf];
+        uint32_t sw[4][2];
 #pragma unroll
-        for (int i = 0; i < D_QK / 16; ++i) dq[i] = zero4;
-        for (int kb = kb_lo; kb <= kb_hi; ++kb) {
-            const int k0 = kb * BW_T, n_valid = min(BW_T, T - k0);
-            __syncthreads();
-            bw_load_tile(Ks, BW_QROW, kseq + (long)k0 * kv_qs, kv_qs, n_valid, D_QK);
-            bw_load_tile(Vs, BW_VROW, vseq + (long)k0 * kv_vs, kv_vs, n_valid, D_V);
-            __syncthreads();
-            uint32_t sw[4][2];
+        for (int k4 = 0; k4 < 4; ++k4) {
+            const __bf16 *ka = ks_ + (16 * k4 + r) * BW_QROW + 8 * g;
+            const __bf16 *va = vs_ + (16 * k4 + r) * BW_VROW + 8 * g;
+            f32x4 stv = zero4, dpt = zero4;
 #pragma unroll
-            for (int k4 = 0; k4 < 4; ++k4) {
-                const __bf16 *ka = Ks + (16 * k4 + r) * BW_QROW + 8 * g;
-                const __bf16 *va = Vs + (16 * k4 + r) * BW_VROW + 8 * g;
-                f32x4 st = zero4, dpt = zero4;
+            for (int kk = 0; kk < D_QK / 32; ++kk)
+                stv = mfma16(*reinterpret_cast<const bf16x8 *>(ka + 32 * kk), qf[kk], stv);
 #pragma unroll
-                for (int kk = 0; kk < D_QK / 32; ++kk)
-                    st = mfma16(*reinterpret_cast<const bf16x8 *>(ka + 32 * kk), qf[kk], st);
+            for (int kk = 0; kk < D_V / 32; ++kk)
+                dpt = mfma16(*reinterpret_cast<const bf16x8 *>(va + 32 * kk), hf[kk], dpt);
+            float dsv[4];
 #pragma unroll
-                for (int kk = 0; kk < D_V / 32; ++kk)
-                    dpt = mfma16(*reinterpret_cast<const bf16x8 *>(va + 32 * kk), hf[kk], dpt);
-                float dsv[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int key = k0 + 16 * k4 + 4 * g + e;
-                    const bool vis = bw_visible(q, key, T, p.window);
-                    const float pv = vis ? fast_exp2(fmaf(st[e], p.scale_log2, -lse)) : 0.f;
-                    dsv[e] = pv * (dpt[e] - dl);
-                }
-                sw[k4][0] = pack_bf16x2(dsv[0], dsv[1]);
-                sw[k4][1] = pack_bf16x2(dsv[2], dsv[3]);
+            for (int e = 0; e < 4; ++e) {
+                const int key = k0 + 16 * k4 + 4 * g + e;
+                const float x = fast_exp2(fmaf(stv[e], p.scale_log2, -lse));
+                const float pv = bw_visible(q, key, T, p.window) ? x : 0.f;
+                dsv[e] = pv * (dpt[e] - dl);
             }
-            // dQ^T += K^T dS^T over the key pairs (blocks 2i, 2i+1)
-#pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const bf16x8 sb = __builtin_bit_cast(bf16x8, (u32x4{sw[2 * i][0], sw[2 * i][1], sw[2 * i + 1][0],
-                                                                    sw[2 * i + 1][1]}));
-#pragma unroll
-                for (int db = 0; db < D_QK / 16; ++db) dq[db] = mfma16(bw_tr_a(Ks, BW_QROW, 32 * i, 16 * db, r, g), sb, dq[db]);
-            }
+            sw[k4][0] = pack_bf16x2(dsv[0], dsv[1]);
+            sw[k4][1] = pack_bf16x2(dsv[2], dsv[3]);
         }
-        // lane (r, g) holds dQ[query r][16db + 4g + e] / scale
-        if (q_ok) {
+        // dQ^T += K^T dS^T over the key pairs (blocks 2i, 2i+1)
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const bf16x8 sb = __builtin_bit_cast(bf16x8, (u32x4{sw[2 * i][0], sw[2 * i][1], sw[2 * i + 1][0],
+                                                                sw[2 * i + 1][1]}));
+#pragma unroll
+            for (int db = 0; db < D_QK / 16; ++db) dq[db] = mfma16(bw_tr_a(ks_, BW_QROW, 32 * i, 16 * db, r, g), sb, dq[db]);
+        }
+        if (it % n_kb == n_kb - 1 && q_ok) {
+            // the head's last key block: lane (r, g) holds dQ[query r][16db + 4g + e] / scale
             __bf16 *dst = h < GROUP ? p.dqs + (((long)b * T + q) * (p.n_kv * GROUP) + GROUP * j + h) * D_QK
                                     : p.dqn + (((long)b * T + q) * p.n_kv + j) * D_QK;
 #pragma unroll
@@ -355,6 +424,8 @@ __global__ __launch_bounds__(BW_THREADS) void bwd_dq_kernel(BwdParams p) {
                     u32x2{pack_bf16x2(dq[db][0] * p.scale, dq[db][1] * p.scale),
                           pack_bf16x2(dq[db][2] * p.scale, dq[db][3] * p.scale)};
         }
+        if (it + 1 < n_steps) st.store(Ks[buf ^ 1], BW_QROW, Vs[buf ^ 1], BW_VROW);
+        __syncthreads();
     }
 }
 
@@ -419,9 +490,9 @@ hipError_t launch_backward(const void *qs, const void *qn, const void *k, const 
     hipLaunchKernelGGL(bwd_pre_kernel, dim3((unsigned)((units + 7) / 8)), dim3(BW_THREADS), 0, stream, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const unsigned n_t = (unsigned)((T + BW_T - 1) / BW_T);
-    hipLaunchKernelGGL(bwd_dkdv_kernel, dim3(n_t, n_kv, B), dim3(BW_THREADS), 0, stream, p);
+    hipLaunchKernelGGL(bwd_dkdv_kernel, dim3(n_kv, n_t, B), dim3(BW_THREADS), 0, stream, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(bwd_dq_kernel, dim3(n_t, n_kv, B), dim3(BW_THREADS), 0, stream, p);
+    hipLaunchKernelGGL(bwd_dq_kernel, dim3(n_kv, n_t, B), dim3(BW_THREADS), 0, stream, p);
     return hipGetLastError();
 }
 

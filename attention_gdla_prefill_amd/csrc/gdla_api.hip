@@ -315,6 +315,7 @@ extern "C" int gdla_prefill_backward(const void *q_signal, const void *q_noise, 
     if (int rc = check_scale_window(softmax_scale, window)) return rc;
     if (B == 0 || T == 0) return GDLA_OK;
     if (B > 65535 || n_kv > 65535) return fail(GDLA_ERR_INVALID_ARG, "B and n_kv must be <= 65535");
+    if (T > 65535 * 64) return fail(GDLA_ERR_INVALID_ARG, "T must be <= 65535 * 64 (the 64-token tiles of a grid dimension)");
 
     const void *ptrs[13] = {q_signal, q_noise, k, v, lambda_, gate, d_out, dq_signal, dq_noise, dk, dv, dlambda,
                             dgate};

@@ -281,7 +281,8 @@ size_t gdla_prefill_backward_workspace_size(int B, int T, int n_kv);
  * contents ignored; calls sharing one must be ordered on one stream.
  * Products are bf16 with fp32 accumulation; P and dS are rounded to bf16
  * before the products that take them.  B = 0 or T = 0 is a valid empty call;
- * B and n_kv must be <= 65535.  Shape support as for gdla_prefill.
+ * B and n_kv must be <= 65535 and T <= 65535 * 64.  Shape support as for
+ * gdla_prefill.
  */
 int gdla_prefill_backward(const void *q_signal, const void *q_noise, const void *k, const void *v,
                           const void *lambda_, const void *gate, const void *d_out, void *dq_signal,

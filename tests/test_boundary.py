@@ -262,6 +262,7 @@ def test_backward_rejections(lib):
     assert backward(lib, window=-1) == INVALID
     assert backward(lib, scale=0.0) == INVALID
     assert backward(lib, B=70000) == INVALID
+    assert backward(lib, T=65535 * 64 + 1, n_kv=1) == INVALID
     for i in range(13):
         ptrs = [A + k * (1 << 36) for k in range(13)]
         ptrs[i] = None
