@@ -61,7 +61,9 @@ struct LatentParams {
     float *part_ml;          // workspace: [B][n_split][n_q][2]  (m in log2 units, l)
     float *part_o;           // workspace: [B][n_split][n_q][512]
     int32_t *redo;           // workspace: [B][n_split][n_hg] chunk needs the exact-maxima redo
+    int32_t *order;          // workspace: [B] sequences by visible length, longest first
     int B, n_kv, n_split, window;
+    int sorted;              // the split kernels take sequence order[blockIdx.y] (B <= LT_SORT_MAX)
     float scale_log2;
 };
 
@@ -72,11 +74,34 @@ struct LatentParams {
 constexpr int LT_ABS_SEQ = 1;
 constexpr int LT_ABS_ROWS = LT_ABS_SEQ * HEADS;     // 5 query rows per workgroup
 constexpr int LT_ABS_THREADS = LT_C / 2;
+constexpr int LT_SORT_MAX = 4096;     // batches up to this size are dispatched longest first
+
+__device__ __forceinline__ int lt_visible(const LatentParams &p, int b) {
+    const int L = p.cu[b + 1] - p.cu[b];
+    return p.window > 0 ? min(L, p.window) : L;
+}
 
 __global__ __launch_bounds__(LT_ABS_THREADS) void latent_absorb_kernel(LatentParams p) {
     __shared__ __attribute__((aligned(16))) float qc[LT_ABS_ROWS][LT_KC];
+    __shared__ int n_longer;
     const int j = blockIdx.x, b0 = blockIdx.y * LT_ABS_SEQ, t = threadIdx.x;
     const int n_sig = p.n_kv * GROUP, n_q = n_sig + p.n_kv;
+    if (p.sorted && j == 0) {
+        // the rank of sequence b0 by visible length, longest first (ties by
+        // index): the split kernels work through the long chunks first, so the
+        // short ones fill the tail
+        if (t == 0) n_longer = 0;
+        __syncthreads();
+        const int mine = lt_visible(p, b0);
+        int c = 0;
+        for (int o = t; o < p.B; o += LT_ABS_THREADS) {
+            const int v = lt_visible(p, o);
+            c += (v > mine || (v == mine && o < b0)) ? 1 : 0;
+        }
+        atomicAdd(&n_longer, c);
+        __syncthreads();
+        if (t == 0) p.order[n_longer] = b0;
+    }
     auto q_src = [&](int b, int h) {
         return h < GROUP ? p.qs + ((long)b * n_sig + GROUP * j + h) * D_QK : p.qn + ((long)b * p.n_kv + j) * D_QK;
     };
@@ -338,7 +363,8 @@ __global__ __launch_bounds__(LT_THREADS, 1) void latent_split_kernel(LatentParam
     __shared__ __attribute__((aligned(16))) LtPTile Pbuf[2];
     __shared__ int range_bad[LT_WAVES];
 
-    const int sp = blockIdx.x, b = blockIdx.y, hg = blockIdx.z;
+    const int sp = blockIdx.x, hg = blockIdx.z;
+    const int b = p.sorted ? p.order[blockIdx.y] : blockIdx.y;
     int32_t *redo_flag = p.redo + ((long)b * p.n_split + sp) * gridDim.z + hg;
     if (REDO && *(volatile int32_t *)redo_flag == 0) return;
     const int n_sig = p.n_kv * GROUP, n_q = n_sig + p.n_kv;
@@ -541,9 +567,9 @@ int latent_splits(int max_seqlen_k, int window) {
     return (int)std::max(1L, std::min(n, 4096L));
 }
 
-// workspace: absorbed queries | chunk maxima and sums | redo flags | chunk outputs
+// workspace: absorbed queries | chunk maxima and sums | redo flags | sequence order | chunk outputs
 struct LtLayout {
-    size_t qt, ml, redo, o, total;
+    size_t qt, ml, redo, order, o, total;
 };
 static LtLayout latent_layout(int B, int n_kv, int n_split) {
     auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
@@ -553,7 +579,8 @@ static LtLayout latent_layout(int B, int n_kv, int n_split) {
     l.qt = 0;
     l.ml = up((size_t)B * n_q * LT_ROW * 2);
     l.redo = l.ml + up((size_t)B * n_split * n_q * 2 * sizeof(float));
-    l.o = l.redo + up((size_t)B * n_split * n_hg * sizeof(int32_t));
+    l.order = l.redo + up((size_t)B * n_split * n_hg * sizeof(int32_t));
+    l.o = l.order + up((size_t)B * sizeof(int32_t));
     l.total = l.o + (size_t)B * n_split * n_q * LT_C * sizeof(float);
     return l;
 }
@@ -580,6 +607,8 @@ hipError_t launch_decode_latent(const void *qs, const void *qn, const void *lat,
     p.qt = reinterpret_cast<__bf16 *>(ws + lay.qt);
     p.part_ml = reinterpret_cast<float *>(ws + lay.ml);
     p.redo = reinterpret_cast<int32_t *>(ws + lay.redo);
+    p.order = reinterpret_cast<int32_t *>(ws + lay.order);
+    p.sorted = B <= LT_SORT_MAX;
     p.part_o = reinterpret_cast<float *>(ws + lay.o);
     p.B = B;
     p.n_kv = n_kv;
