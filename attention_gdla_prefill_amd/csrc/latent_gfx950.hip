@@ -115,20 +115,23 @@ __global__ __launch_bounds__(LT_ABS_THREADS) void latent_absorb_kernel(LatentPar
 #pragma unroll
     for (int i = 0; i < LT_ABS_ROWS; ++i) acc[i][0] = acc[i][1] = 0.f;
     const uint32_t *w = reinterpret_cast<const uint32_t *>(p.wuk + (long)j * LT_KC * LT_C) + t;
-    for (int d = 0; d < LT_KC; d += 4) {
-        uint32_t wv[4];
+    for (int d0 = 0; d0 < LT_KC; d0 += 16) {
+        // 16 rows of the column pair in flight per round
+        uint32_t wv[16];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) wv[k] = __builtin_nontemporal_load(w + (d + k) * (LT_C / 2));
+        for (int k = 0; k < 16; ++k) wv[k] = __builtin_nontemporal_load(w + (d0 + k) * (LT_C / 2));
 #pragma unroll
-        for (int i = 0; i < LT_ABS_ROWS; ++i) {
-            const float4 qv = *reinterpret_cast<const float4 *>(&qc[i][d]);
-            const float q4[4] = {qv.x, qv.y, qv.z, qv.w};
+        for (int d = 0; d < 16; d += 4)
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                acc[i][0] = fmaf(q4[k], bf16_lo(wv[k]), acc[i][0]);
-                acc[i][1] = fmaf(q4[k], bf16_hi(wv[k]), acc[i][1]);
+            for (int i = 0; i < LT_ABS_ROWS; ++i) {
+                const float4 qv = *reinterpret_cast<const float4 *>(&qc[i][d0 + d]);
+                const float q4[4] = {qv.x, qv.y, qv.z, qv.w};
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    acc[i][0] = fmaf(q4[k], bf16_lo(wv[d + k]), acc[i][0]);
+                    acc[i][1] = fmaf(q4[k], bf16_hi(wv[d + k]), acc[i][1]);
+                }
             }
-        }
     }
 #pragma unroll
     for (int i = 0; i < LT_ABS_ROWS; ++i) {
