@@ -13,12 +13,15 @@
 //      loads into a ring of three tile slots, two tiles ahead, shared by the
 //      4 waves and all 5 heads; V stays row-major and the P*V operand is read
 //      with the gfx950 LDS transpose read (ds_read_b64_tr_b16);
-//   3. S^T = K Q^T on the matrix cores (bf16 in, fp32 out), causal / window
-//      mask on the tiles that straddle the band edge only;
+//   3. S^T = K Q^T on the matrix cores (bf16 in, fp32 out); the causal /
+//      window mask enters as the products' initial value (0 or -inf) on the
+//      slices that straddle the band edge only;
 //   4. online softmax in base 2 with the scale folded in.  Each row's
-//      reference maximum is fixed by the first visible keys it meets (the
-//      row maximum is not tracked after that), so the accumulators are never
-//      rescaled inside the loop and stay in the matrix-core register file.
+//      reference maximum is fixed before the key loop by the visible keys of
+//      the row's own 16-key block (the row maximum is not tracked after that),
+//      so the accumulators are never rescaled inside the loop and stay in the
+//      matrix-core register file, and every slice runs the same straight-line
+//      code.
 //      Row sums are taken over the same bf16-rounded weights that enter P*V.
 //      If a row's sum ends a query tile far above its reference range (logits
 //      that grew by more than ~40 natural units; rare), the workgroup redoes
@@ -248,130 +251,179 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_kernel(PrefillParams p)
     f32x4 o[HEADS][D_V / 16];
     const float c_log2 = p.scale_log2;
     if (tid < 2) restart_flag[tid] = 0;
-    bool wave_restart = false;        // a row sum of this wave left the reference range
-    bool max_pass = false;            // scores only: exact row maxima become the references
     int n_done = 0;                   // query tiles finished by the workgroup
+    const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
 
-    // ---- one key tile: 2 slices of 32 keys, each S^T = K Q^T, softmax, O^T += V^T P^T
-    auto compute_tile = [&](int kt, const __bf16 *ks, const __bf16 *vs) {
-        // kept rolled: unrolling lets the scheduler overlap two slices, which
-        // doubles the live scores and spills
-#pragma unroll 1
-        for (int sub = 0; sub < 2; ++sub) {
-            const int kb0 = kt * PF_BN + 32 * sub;     // first key of this 32-key slice
-            // wave-uniform skips: no valid query, all keys in the future, all keys too old
-            if (tw >= T || (PREFIX && tw + 15 < P) || kb0 > tw + 15) continue;
-            if (window > 0 && kb0 + 31 < tw - window + 1) continue;
-            const bool need_mask = (kb0 + 31 > tw) || (window > 0 && kb0 < tw + 16 - window);
+    // Masking enters the scores through the products' initial value: 0 for a
+    // visible (key, query) pair, -inf for a hidden one, so a hidden key's weight
+    // is exp2(-inf) = 0 and no branch or select touches the scores.  bias[kb]
+    // covers this lane's keys kb0 + 16 kb + 4g + e (e = 0..3) for its query tq.
+    auto make_bias = [&](int kb0, f32x4 (&bias)[2]) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int key = kb0 + 16 * (i >> 2) + 4 * g + (i & 3);
+            const bool vis = key <= tq && (window == 0 || key > tq - window);
+            bias[i >> 2][i & 3] = vis ? 0.f : -INFINITY;
+        }
+    };
 
-            // S^T = K Q^T, first the 16 keys of block 0 for all heads, then block 1.
-            // The six K fragments of a block are read before its MFMAs.
-            const __bf16 *krd = ks + (32 * sub + r) * KS_ROW + 8 * g;
-            f32x4 s[HEADS][2];
-            const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
-            auto qk_block = [&](int kb) {
-                const __bf16 *kr = krd + 16 * kb * KS_ROW;
-                bf16x8 kf[KK_STEPS];
+    // ---- the reference of each row (log2 units): the largest score over the
+    // visible keys of the row's own 16-key block (key tq is always visible).
+    // K rows tw .. tw+15 come straight from global memory as A fragments.
+    auto ref_pass = [&]() {
+        const int key = tw + r;
+        const bool ok = key < T;
+        const __bf16 *krow = p.k + ((kseq0 + (ok ? key : 0)) * n_kv + j) * D_QK + 8 * g;
+        bf16x8 kf[KK_STEPS];
 #pragma unroll
-                for (int kk = 0; kk < KK_STEPS; ++kk) kf[kk] = *reinterpret_cast<const bf16x8 *>(kr + 32 * kk);
+        for (int kk = 0; kk < KK_STEPS; ++kk) {
+            const u32x4 w = ok ? ldg16(krow + 32 * kk) : u32x4{0, 0, 0, 0};
+            kf[kk] = __builtin_bit_cast(bf16x8, w);
+        }
+        f32x4 bias[2];
+        make_bias(tw, bias);          // block 0 of a slice starting at key tw
+        f32x4 sd[HEADS];
 #pragma unroll
-                for (int kk = 0; kk < KK_STEPS; ++kk)
+        for (int kk = 0; kk < KK_STEPS; ++kk)
 #pragma unroll
-                    for (int h = 0; h < HEADS; ++h)
-                        s[h][kb] = mfma16(kf[kk], qf[h][kk], kk == 0 ? zero4 : s[h][kb]);
-            };
-            // weights of key block kb against the fixed references: p = 2^(x*c - ref)
-            uint32_t pw[HEADS][4];
-            auto weights = [&](int kb, unsigned vis) {
+            for (int h = 0; h < HEADS; ++h) sd[h] = mfma16(kf[kk], qf[h][kk], kk == 0 ? bias[0] : sd[h]);
 #pragma unroll
-                for (int h = 0; h < HEADS; ++h) {
-                    const float mref = m_ref[h] == -INFINITY ? 0.f : m_ref[h];
-                    float pv[4];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        pv[e] = fast_exp2(fmaf(s[h][kb][e], c_log2, -mref));
-                        pv[e] = (vis >> (4 * kb + e)) & 1 ? pv[e] : 0.f;
-                    }
-                    pw[h][2 * kb] = pack_bf16x2(pv[0], pv[1]);
-                    pw[h][2 * kb + 1] = pack_bf16x2(pv[2], pv[3]);
-                }
-            };
+        for (int h = 0; h < HEADS; ++h) {
+            const float mx = fmaxf(fmaxf(sd[h][0], sd[h][1]), fmaxf(sd[h][2], sd[h][3]));
+            m_ref[h] = group4_max(mx) * c_log2;
+        }
+    };
 
-            // visibility of this lane's 8 keys kb0 + 16*(i/4) + 4g + i%4 (edge slices only)
-            unsigned vis = 0xffu;
-            if (need_mask) {
-                vis = 0;
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const int key = kb0 + 16 * (i >> 2) + 4 * g + (i & 3);
-                    if (key <= tq && (window == 0 || key > tq - window)) vis |= 1u << i;
-                }
-            }
-            // largest visible score of this lane's row, in log2 units
-            auto row_max = [&](int h) {
-                float mx = -INFINITY;
-#pragma unroll
-                for (int i = 0; i < 8; ++i)
-                    mx = fmaxf(mx, (vis >> i) & 1 ? s[h][i >> 2][i & 3] : -INFINITY);
-                return group4_max(mx) * c_log2;
-            };
+    // slice-level skips (wave-uniform): no valid query, all keys in the future,
+    // all keys too old; and whether a slice needs masking at all
+    auto slice_skipped = [&](int kb0) {
+        return tw >= T || (PREFIX && tw + 15 < P) || kb0 > tw + 15 ||
+               (window > 0 && kb0 + 31 < tw - window + 1);
+    };
+    auto slice_masked = [&](int kb0) {
+        return (kb0 + 31 > tw) || (window > 0 && kb0 < tw + 16 - window);
+    };
 
-            bool unset = false;
+    // ---- one 32-key slice: S^T = K Q^T, weights against the fixed references,
+    // O^T += V^T P^T.  Straight-line code (one basic block from the first K read
+    // to the last product), so that the exponentials of block 0 overlap the
+    // products of block 1 and those of block 1 the P*V products.
+    auto slice = [&](int sub, const __bf16 *ks, const __bf16 *vs, const f32x4 (&bias)[2]) {
+        const __bf16 *krd = ks + (32 * sub + r) * KS_ROW + 8 * g;
+        f32x4 s[HEADS][2];
+        uint32_t pw[HEADS][4];
 #pragma unroll
-            for (int h = 0; h < HEADS; ++h) unset |= m_ref[h] == -INFINITY;
-            if (!need_mask && !__any(unset) && !max_pass) {
-                // common case: every key visible, every reference set; one basic
-                // block, so block 0's exponentials overlap block 1's MFMAs
-                qk_block(0);
-                weights(0, 0xffu);
-                qk_block(1);
-                weights(1, 0xffu);
-            } else {
-                // band edge, rows without a reference yet, or the scores-only pass
-                qk_block(0);
-                qk_block(1);
+        for (int kb = 0; kb < 2; ++kb) {
+            const __bf16 *kr = krd + 16 * kb * KS_ROW;
+            bf16x8 kf[KK_STEPS];
 #pragma unroll
-                for (int h = 0; h < HEADS; ++h) {
-                    if (max_pass || __any(m_ref[h] == -INFINITY)) {
-                        const float mx = row_max(h);
-                        if (max_pass || m_ref[h] == -INFINITY) m_ref[h] = fmaxf(m_ref[h], mx);
-                    }
-                }
-                if (max_pass) continue;
-                weights(0, vis);
-                weights(1, vis);
-            }
-
-            bf16x8 pb[HEADS];
+            for (int kk = 0; kk < KK_STEPS; ++kk) kf[kk] = *reinterpret_cast<const bf16x8 *>(kr + 32 * kk);
+#pragma unroll
+            for (int kk = 0; kk < KK_STEPS; ++kk)
+#pragma unroll
+                for (int h = 0; h < HEADS; ++h) s[h][kb] = mfma16(kf[kk], qf[h][kk], kk == 0 ? bias[kb] : s[h][kb]);
 #pragma unroll
             for (int h = 0; h < HEADS; ++h) {
-                const u32x4 w = {pw[h][0], pw[h][1], pw[h][2], pw[h][3]};
-                pb[h] = __builtin_bit_cast(bf16x8, w);
+                float pv[4];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) l_part[h] = sum_bf16x2(pw[h][i], l_part[h]);
-            }
-
-            // O^T += V^T P^T.  The A operand (16 columns c x 32 keys) comes from
-            // two transposing reads of row-major V: lane (r, g) receives
-            // V[4g + e][16cb + r] and V[16 + 4g + e][16cb + r], e = 0..3 -- the
-            // keys its P^T fragment holds in k-slots 8g..8g+7.
-            const __bf16 *vrd = vs + (32 * sub + 4 * g + (r >> 2)) * VS_ROW + 4 * (r & 3);
-            auto vfrag = [&](int cb) {
-                const s16x4 lo = lds_read_tr16(vrd + 16 * cb);
-                const s16x4 hi4 = lds_read_tr16(vrd + 16 * VS_ROW + 16 * cb);
-                const s16x4 v8[2] = {lo, hi4};
-                return __builtin_bit_cast(bf16x8, v8);
-            };
-            bf16x8 va = vfrag(0);
-#pragma unroll
-            for (int cb = 0; cb < D_V / 16; ++cb) {
-                bf16x8 nv = va;
-                if (cb + 1 < D_V / 16) nv = vfrag(cb + 1);
-#pragma unroll
-                for (int h = 0; h < HEADS; ++h) o[h][cb] = mfma16(va, pb[h], o[h][cb]);
-                va = nv;
+                for (int e = 0; e < 4; ++e) pv[e] = fast_exp2(fmaf(s[h][kb][e], c_log2, -m_ref[h]));
+                pw[h][2 * kb] = pack_bf16x2(pv[0], pv[1]);
+                pw[h][2 * kb + 1] = pack_bf16x2(pv[2], pv[3]);
             }
         }
+        bf16x8 pb[HEADS];
+#pragma unroll
+        for (int h = 0; h < HEADS; ++h) {
+            const u32x4 w = {pw[h][0], pw[h][1], pw[h][2], pw[h][3]};
+            pb[h] = __builtin_bit_cast(bf16x8, w);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) l_part[h] = sum_bf16x2(pw[h][i], l_part[h]);
+        }
+        // O^T += V^T P^T.  The A operand (16 columns c x 32 keys) comes from
+        // two transposing reads of row-major V: lane (r, g) receives
+        // V[4g + e][16cb + r] and V[16 + 4g + e][16cb + r], e = 0..3 -- the
+        // keys its P^T fragment holds in k-slots 8g..8g+7.
+        const __bf16 *vrd = vs + (32 * sub + 4 * g + (r >> 2)) * VS_ROW + 4 * (r & 3);
+        auto vfrag = [&](int cb) {
+            const s16x4 lo = lds_read_tr16(vrd + 16 * cb);
+            const s16x4 hi4 = lds_read_tr16(vrd + 16 * VS_ROW + 16 * cb);
+            const s16x4 v8[2] = {lo, hi4};
+            return __builtin_bit_cast(bf16x8, v8);
+        };
+        bf16x8 va = vfrag(0);
+#pragma unroll
+        for (int cb = 0; cb < D_V / 16; ++cb) {
+            bf16x8 nv = va;
+            if (cb + 1 < D_V / 16) nv = vfrag(cb + 1);
+#pragma unroll
+            for (int h = 0; h < HEADS; ++h) o[h][cb] = mfma16(va, pb[h], o[h][cb]);
+            va = nv;
+        }
+    };
+
+    // scores only (the redo's first pass): exact row maxima over the visible keys
+    auto max_slice = [&](int sub, const __bf16 *ks, const f32x4 (&bias)[2]) {
+        const __bf16 *krd = ks + (32 * sub + r) * KS_ROW + 8 * g;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            const __bf16 *kr = krd + 16 * kb * KS_ROW;
+            bf16x8 kf[KK_STEPS];
+#pragma unroll
+            for (int kk = 0; kk < KK_STEPS; ++kk) kf[kk] = *reinterpret_cast<const bf16x8 *>(kr + 32 * kk);
+            f32x4 sb[HEADS];
+#pragma unroll
+            for (int kk = 0; kk < KK_STEPS; ++kk)
+#pragma unroll
+                for (int h = 0; h < HEADS; ++h) sb[h] = mfma16(kf[kk], qf[h][kk], kk == 0 ? bias[kb] : sb[h]);
+#pragma unroll
+            for (int h = 0; h < HEADS; ++h) {
+                const float mx = fmaxf(fmaxf(sb[h][0], sb[h][1]), fmaxf(sb[h][2], sb[h][3]));
+                m_ref[h] = fmaxf(m_ref[h], group4_max(mx) * c_log2);
+            }
+        }
+    };
+
+    // ---- the key tiles of query tile qt.  MODE 0: the normal pass (checks the
+    // row sums at the end), 1: scores only, 2: the normal pass after it (the
+    // references are exact maxima: every weight <= 1).  Before each barrier a
+    // wave drains its older copies and all LDS traffic but may leave its newest
+    // batch (13 or 14 copies) in flight when the tile computed next is older
+    // than it.  The barrier is the bare s_barrier: a workgroup fence would also
+    // drain the newest copies.  Returns whether any wave asked for the redo.
+    auto run_tiles = [&](int qt, int kt_lo, int kt_hi, int next_lo, const int mode) {
+        bool wave_restart = false;
+        for (int kt = kt_lo; kt <= kt_hi; ++kt) {
+            const __bf16 *ks = Kring[kt % 3], *vs = Vring[kt % 3];
+            // kept rolled: unrolling lets the scheduler overlap two slices,
+            // which doubles the live scores and spills
+#pragma unroll 1
+            for (int sub = 0; sub < 2; ++sub) {
+                const int kb0 = kt * PF_BN + 32 * sub;
+                if (slice_skipped(kb0)) continue;
+                f32x4 bias[2];
+                if (slice_masked(kb0)) make_bias(kb0, bias);
+                else bias[0] = bias[1] = zero4;
+                if (mode == 1) max_slice(sub, ks, bias);
+                else slice(sub, ks, vs, bias);
+            }
+            const bool last = kt == kt_hi;
+            if (last && mode == 0 && (!PREFIX || tq >= P) && tq < T) {
+#pragma unroll
+                for (int h = 0; h < HEADS; ++h) wave_restart |= !(l_part[h] <= RESTART_PART_SUM);
+            }
+            // the redo passes end where the normal pass ended: the same copies
+            // for the query tile that follows
+            const int nt = !last ? kt + 1 : (mode == 1 ? kt_lo : next_lo);   // tile computed next
+            const int limit = min(min(kt, nt) + 2, mode == 1 ? kt_hi : run_last_tile);
+            while (next_copy <= limit) issue_tile(next_copy++);
+            if (last && mode == 0 && __any(wave_restart) && lane == 0) restart_flag[n_done & 1] = 1;
+            if (next_copy - 1 > nt) __builtin_amdgcn_s_waitcnt(0x007D);   // vmcnt(13) lgkmcnt(0)
+            else __builtin_amdgcn_s_waitcnt(0x0070);                      // vmcnt(0) lgkmcnt(0)
+            asm volatile("" ::: "memory");                                // no compiler motion across
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+        }
+        return mode == 0 && __builtin_amdgcn_readfirstlane(restart_flag[n_done & 1]) != 0;
     };
 
     wait_vmem();
@@ -386,65 +438,38 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_kernel(PrefillParams p)
         const int next_lo = qt + 1 < qt_end ? tile_lo(qt + 1) : 1 << 30;
 #pragma unroll
         for (int h = 0; h < HEADS; ++h) {
-            m_ref[h] = -INFINITY;
             l_part[h] = 0.f;
 #pragma unroll
-            for (int cb = 0; cb < D_V / 16; ++cb) o[h][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int cb = 0; cb < D_V / 16; ++cb) o[h][cb] = zero4;
         }
-
-        // ---- the key-tile loop.  Before each barrier a wave drains its older
-        // copies and all LDS traffic but may leave its newest batch (13 or 14
-        // copies) in flight when the tile computed next is older than it.  The
-        // barrier is the bare s_barrier: a workgroup fence would also drain the
-        // newest copies.
-        // The weights are taken against references fixed by each row's first
-        // visible keys.  If a lane's part of a row sum ends above 2^62 (or is
-        // not finite), the workgroup redoes the query tile in two passes: scores
-        // only, for the exact row maxima, then the normal pass with those as
-        // references (every weight <= 1, so no sum comes near 2^62).
-        bool exact = false;           // references are exact maxima: no further check
-        int kt = kt_lo;
-        while (kt <= kt_hi) {
-            compute_tile(kt, Kring[kt % 3], Vring[kt % 3]);
-            const bool last = kt == kt_hi;
-            if (last && !max_pass && !exact && (!PREFIX || tq >= P) && tq < T) {
+        // The weights are taken against the references of ref_pass.  If a
+        // lane's part of a row sum ends above 2^62 (or is not finite), the
+        // workgroup redoes the query tile in two passes: scores only, for the
+        // exact row maxima, then the normal pass with those as references
+        // (every weight <= 1, so no sum comes near 2^62).
+        ref_pass();
+        if (run_tiles(qt, kt_lo, kt_hi, next_lo, 0)) {
+            wait_vmem();
+            __syncthreads();                   // every wave has read the flag
+            if (tid == 0) restart_flag[n_done & 1] = 0;
 #pragma unroll
-                for (int h = 0; h < HEADS; ++h) wave_restart |= !(l_part[h] <= RESTART_PART_SUM);
+            for (int h = 0; h < HEADS; ++h) m_ref[h] = -INFINITY;
+            start_ring(qt);
+            wait_vmem();
+            __syncthreads();
+            run_tiles(qt, kt_lo, kt_hi, next_lo, 1);
+#pragma unroll
+            for (int h = 0; h < HEADS; ++h) {
+                l_part[h] = 0.f;
+#pragma unroll
+                for (int cb = 0; cb < D_V / 16; ++cb) o[h][cb] = zero4;
             }
-            const int nt = !last ? kt + 1 : next_lo;    // tile computed next
-            const int limit = min(min(kt, nt) + 2, run_last_tile);
-            while (next_copy <= limit) issue_tile(next_copy++);
-            if (last && __any(wave_restart) && lane == 0) restart_flag[n_done & 1] = 1;
-            if (next_copy - 1 > nt) __builtin_amdgcn_s_waitcnt(0x007D);   // vmcnt(13) lgkmcnt(0)
-            else __builtin_amdgcn_s_waitcnt(0x0070);                      // vmcnt(0) lgkmcnt(0)
-            asm volatile("" ::: "memory");                                // no compiler motion across
-            __builtin_amdgcn_s_barrier();
-            asm volatile("" ::: "memory");
-            if (last && (max_pass || (!exact && __builtin_amdgcn_readfirstlane(restart_flag[n_done & 1])))) {
-                // start the scores-only pass, or the normal pass after it
-                wait_vmem();
-                __syncthreads();                   // every wave has read the flag
-                if (tid == 0) restart_flag[n_done & 1] = 0;
-                if (!max_pass) {
-#pragma unroll
-                    for (int h = 0; h < HEADS; ++h) m_ref[h] = -INFINITY;
-                }
-#pragma unroll
-                for (int h = 0; h < HEADS; ++h) {
-                    l_part[h] = 0.f;
-#pragma unroll
-                    for (int cb = 0; cb < D_V / 16; ++cb) o[h][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
-                }
-                exact = max_pass;
-                max_pass = !max_pass;
-                wave_restart = false;
-                start_ring(qt);
-                wait_vmem();
-                __syncthreads();
-                kt = kt_lo;
-                continue;
-            }
-            ++kt;
+            wait_vmem();
+            __syncthreads();
+            start_ring(qt);
+            wait_vmem();
+            __syncthreads();
+            run_tiles(qt, kt_lo, kt_hi, next_lo, 2);
         }
         ++n_done;
 

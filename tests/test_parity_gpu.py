@@ -73,19 +73,26 @@ def test_prefill_parity_small(B, T, n_kv, window, dist):
     compare(gpu_prefill(x, window), oracle_prefill(x, window), "B%d T%d W%d %s" % (B, T, window, dist))
 
 
-def test_prefill_growing_logits_restart():
-    """Scores that grow by ~92 log2 units per 32 keys: the per-row reference
-    must be raised mid-pass (the restart path) for the result to stay right."""
+@pytest.mark.parametrize("direction", ["growing", "shrinking"])
+def test_prefill_steep_logits_restart(direction):
+    """Scores that change by ~92 log2 units per 32 keys.  Each row's reference
+    comes from its own 16-key block: growing scores peak there, shrinking ones
+    peak at the oldest visible key, so their weights would overflow against that
+    reference and the query tile must be redone against its exact row maxima
+    (the restart path) for the result to stay right."""
     B, T, n_kv = 1, 256, 2
-    log("prefill restart path T=256")
+    log("prefill restart path T=256 %s" % direction)
     x = W.prefill_inputs(small(B, T, n_kv), seed=5, **SHARP)
     x["q_signal"][..., 0] = 16.0
     x["q_noise"][..., 0] = 16.0
-    x["k"][0, :, :, 0] = (torch.arange(T, dtype=torch.float32) / 8).to(torch.bfloat16)[:, None]
+    pos = torch.arange(T, dtype=torch.float32)
+    if direction == "shrinking":
+        pos = T - pos
+    x["k"][0, :, :, 0] = (pos / 8).to(torch.bfloat16)[:, None]
     x = to_dev(x)
     for window in (0, 100):
         compare(gpu_prefill(x, window, scale=1.0), oracle_prefill(x, window, scale=1.0),
-                "restart W%d" % window)
+                "restart %s W%d" % (direction, window))
 
 
 def test_prefill_lambda_one_identical_queries_near_zero():
