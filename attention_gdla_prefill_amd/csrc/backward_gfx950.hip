@@ -64,43 +64,67 @@ __device__ __forceinline__ bf16x8 bw_tr_a(const __bf16 *m, int rs, int row0, int
 }
 
 
-// A 64-row tile pair staged through registers: the global loads of the next
-// step are issued before the current step computes and land in the other LDS
-// buffer after it, so the copy runs under the products.  Thread t holds
-// chunks t, t+256, .. of the first tile (cols_a values per row) and of the
-// second (cols_b), 16 bytes each.
-template <int COLS_A, int COLS_B>
-struct BwStage {
-    static constexpr int NA = BW_T * COLS_A / 8 / BW_THREADS, NB = BW_T * COLS_B / 8 / BW_THREADS;
-    u32x4 a[NA], b[NB];
-    float x0, x1;                          // two per-row scalars (threads < 64)
-    __device__ __forceinline__ void load(const __bf16 *sa, long gsa, const __bf16 *sb, long gsb, int n_valid) {
-        const u32x4 z = {0, 0, 0, 0};
-#pragma unroll
-        for (int i = 0; i < NA; ++i) {
-            const int c = threadIdx.x + BW_THREADS * i, row = c / (COLS_A / 8), col = (c % (COLS_A / 8)) * 8;
-            a[i] = row < n_valid ? ldg16(sa + row * gsa + col) : z;
-        }
-#pragma unroll
-        for (int i = 0; i < NB; ++i) {
-            const int c = threadIdx.x + BW_THREADS * i, row = c / (COLS_B / 8), col = (c % (COLS_B / 8)) * 8;
-            b[i] = row < n_valid ? ldg16(sb + row * gsb + col) : z;
-        }
+// ---- 64-row tiles are copied HBM -> LDS with direct (register-free) 16-byte
+// loads into a ring of three slots, two steps ahead of the step that reads
+// them.  The copy is written as a statement the compiler does not model as an
+// LDS write: otherwise it waits for every copy in flight before the next LDS
+// read, which would leave no copy in flight under the products.  The kernels
+// order copies and reads themselves (vmcnt waits and a barrier before a slot
+// is read, and a slot is refilled only after the barrier that ends its last
+// reader).  Lane l of a copy writes lds_addr + size*l; the LDS address goes to
+// M0; the nop is the wait state an LDS-DMA load needs after M0 is written.
+typedef int bw_i32x4 __attribute__((ext_vector_type(4)));
+
+// raw buffer resource over `bytes` bytes from `base`: reads at byte offsets
+// >= bytes return zeros (rows past the sequence end)
+__device__ __forceinline__ bw_i32x4 bw_rsrc(const void *base, uint32_t bytes) {
+    const uint64_t a = (uint64_t)(uintptr_t)base;
+    return bw_i32x4{(int)(uint32_t)a, (int)(uint32_t)(a >> 32), (int)bytes, 0x00020000};
+}
+__device__ __forceinline__ void bw_copy16(const bw_i32x4 &rsrc, uint32_t byte_off, uint32_t lds_addr) {
+    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                 :: "v"(byte_off), "s"(rsrc), "{m0}"(lds_addr) : "memory");
+}
+__device__ __forceinline__ void bw_copy4(const bw_i32x4 &rsrc, uint32_t byte_off, uint32_t lds_addr) {
+    asm volatile("s_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds"
+                 :: "v"(byte_off), "s"(rsrc), "{m0}"(lds_addr) : "memory");
+}
+template <typename T>
+__device__ __forceinline__ uint32_t bw_lds(const T *p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) T *)p;
+}
+
+// One 64-row tile of COLS bf16 per row into LDS rows of RS bf16 (RS - COLS
+// pad): each copy instruction covers whole rows (2 rows of 26 chunks for the
+// 192-wide tiles, 3 rows of 18 chunks for the 128-wide ones), so a lane's row
+// and chunk within an instruction are fixed and the pad chunks are skipped;
+// wave w issues instructions w, w+4, ...
+template <int COLS, int RS>
+struct BwTileCopy {
+    static constexpr int CH = RS / 8;                 // 16-byte chunks per LDS row
+    static constexpr int ROWS = 64 / CH;              // rows per instruction
+    static constexpr int N = (BW_T + ROWS - 1) / ROWS;
+    static constexpr int PER_WAVE = (N + 3) / 4;
+    int lr, ch;
+    __device__ __forceinline__ void init(int lane) {
+        lr = lane / CH;
+        ch = lane % CH;
     }
-    __device__ __forceinline__ void store(__bf16 *la, int lsa, __bf16 *lb, int lsb) const {
+    // rows of the tile start at `rsrc`, `row_bytes` apart; lds_tile: LDS byte address of the slot
+    __device__ __forceinline__ void issue(const bw_i32x4 &rsrc, uint32_t row_bytes, uint32_t lds_tile, int wave) const {
 #pragma unroll
-        for (int i = 0; i < NA; ++i) {
-            const int c = threadIdx.x + BW_THREADS * i, row = c / (COLS_A / 8), col = (c % (COLS_A / 8)) * 8;
-            *reinterpret_cast<u32x4 *>(la + row * lsa + col) = a[i];
-        }
-#pragma unroll
-        for (int i = 0; i < NB; ++i) {
-            const int c = threadIdx.x + BW_THREADS * i, row = c / (COLS_B / 8), col = (c % (COLS_B / 8)) * 8;
-            *reinterpret_cast<u32x4 *>(lb + row * lsb + col) = b[i];
+        for (int c = 0; c < PER_WAVE; ++c) {
+            const int row0 = ROWS * (wave + 4 * c);
+            if (row0 < BW_T && lr < ROWS && ch < COLS / 8 && row0 + lr < BW_T)
+                bw_copy16(rsrc, (uint32_t)(row0 + lr) * row_bytes + 16 * ch, lds_tile + (uint32_t)(row0 * RS * 2));
         }
     }
 };
-static_assert(BW_T * D_QK / 8 % BW_THREADS == 0 && BW_T * D_V / 8 % BW_THREADS == 0, "tile chunks per thread");
+static_assert(64 / (BW_QROW / 8) == 2 && 64 / (BW_VROW / 8) == 3, "rows per copy");
+// copies one wave issues per step, at least: 8 of a 192-wide tile, 5 of a
+// 128-wide one; the wait at a step's end leaves this many (the next step's
+// copies, issued last) in flight
+constexpr int BW_STEP_COPIES_MIN = 13;
 
 __device__ __forceinline__ bool bw_visible(int q, int key, int T, int window) {
     return q < T && key <= q && (window == 0 || q - key < window);
@@ -193,13 +217,14 @@ __device__ __forceinline__ BwHead bw_head(const BwdParams &p, int b, int j, int 
 
 // ---- 2. dK, dV.  Workgroup (KV head j, 64-key block, sequence b); wave w owns
 // keys kb0 + 16w .. +15.  Steps: (query tile, head) for every query tile that
-// sees a key of the block and each of the 5 heads; the Q and dH tiles of the
-// next step are copied while the current one computes (two LDS buffers).  In C
-// layout lane (r, g) holds element [query 16qb + 4g + e][key r] of S, P, dP, dS.
+// sees a key of the block and each of the 5 heads; the Q and dH tiles, the
+// log2-sum-exp and delta of a step are copied two steps ahead into a ring of
+// three LDS slots.  In C layout lane (r, g) holds element [query 16qb + 4g + e]
+// [key r] of S, P, dP, dS.
 __global__ __launch_bounds__(BW_THREADS, 1) void bwd_dkdv_kernel(BwdParams p) {
-    __shared__ __attribute__((aligned(16))) __bf16 Qs[2][BW_T * BW_QROW];
-    __shared__ __attribute__((aligned(16))) __bf16 Hs[2][BW_T * BW_VROW];
-    __shared__ __attribute__((aligned(16))) float lse_s[2][BW_T], dl_s[2][BW_T];
+    __shared__ __attribute__((aligned(16))) __bf16 Qs[3][BW_T * BW_QROW];
+    __shared__ __attribute__((aligned(16))) __bf16 Hs[3][BW_T * BW_VROW];
+    __shared__ __attribute__((aligned(16))) float lse_s[3][BW_T], dl_s[3][BW_T];
     // the KV head is the fastest grid index, so the workgroups are dispatched
     // longest first (key block 0 sees every query tile)
     const int j = blockIdx.x, kb0 = blockIdx.y * BW_T, b = blockIdx.z;
@@ -230,30 +255,30 @@ __global__ __launch_bounds__(BW_THREADS, 1) void bwd_dkdv_kernel(BwdParams p) {
     int qt_hi = (T - 1) / BW_T;
     if (p.window > 0) qt_hi = min(qt_hi, (kb0 + BW_T - 1 + p.window - 1) / BW_T);
     const int n_steps = (qt_hi - qt_lo + 1) * HEADS;
-    BwStage<D_QK, D_V> st;
-    auto fetch = [&](int it) {
-        const int q0 = (qt_lo + it / HEADS) * BW_T, n_valid = min(BW_T, T - q0);
+    BwTileCopy<D_QK, BW_QROW> cq;
+    BwTileCopy<D_V, BW_VROW> ch;
+    cq.init(lane);
+    ch.init(lane);
+    const int uwave = __builtin_amdgcn_readfirstlane(wave);
+    // the copies of step it into slot it % 3
+    auto issue = [&](int it) {
+        const int slot = it % 3, q0 = (qt_lo + it / HEADS) * BW_T, n_valid = min(BW_T, T - q0);
         const BwHead hd = bw_head(p, b, j, it % HEADS);
-        st.load(hd.q + (long)q0 * hd.q_stride, hd.q_stride, hd.dh + (long)q0 * hd.dh_stride, hd.dh_stride, n_valid);
-        if (tid < BW_T) {
-            const long row = (long)b * T + q0 + tid;
-            st.x0 = tid < n_valid ? p.lse[row * n_h + hd.col] : 0.f;
-            st.x1 = tid < n_valid ? p.delta[row * n_h + hd.col] : 0.f;
-        }
+        const uint32_t qrb = (uint32_t)hd.q_stride * 2, hrb = (uint32_t)hd.dh_stride * 2;
+        cq.issue(bw_rsrc(hd.q + (long)q0 * hd.q_stride, (uint32_t)n_valid * qrb), qrb, bw_lds(Qs[slot]), uwave);
+        ch.issue(bw_rsrc(hd.dh + (long)q0 * hd.dh_stride, (uint32_t)n_valid * hrb), hrb, bw_lds(Hs[slot]), uwave);
+        // the rows' log2-sum-exp (wave 0) and delta (wave 1), one float per lane
+        const long row0 = (long)b * T + q0;
+        if (uwave < 2)
+            bw_copy4(bw_rsrc((uwave == 0 ? p.lse : p.delta) + row0 * n_h + hd.col, (uint32_t)(n_valid * n_h * 4)),
+                     (uint32_t)(lane * n_h * 4), uwave == 0 ? bw_lds(lse_s[slot]) : bw_lds(dl_s[slot]));
     };
-    auto stage = [&](int buf) {
-        st.store(Qs[buf], BW_QROW, Hs[buf], BW_VROW);
-        if (tid < BW_T) {
-            lse_s[buf][tid] = st.x0;
-            dl_s[buf][tid] = st.x1;
-        }
-    };
-    fetch(0);
-    stage(0);
+    issue(0);
+    if (n_steps > 1) issue(1);
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
     __syncthreads();
     for (int it = 0; it < n_steps; ++it) {
-        const int buf = it & 1, q0 = (qt_lo + it / HEADS) * BW_T;
-        if (it + 1 < n_steps) fetch(it + 1);
+        const int buf = it % 3, q0 = (qt_lo + it / HEADS) * BW_T;
         const __bf16 *qs_ = Qs[buf], *hs_ = Hs[buf];
         // S = Q K_w^T and dP = dH V_w^T, four 16-query blocks
         f32x4 s[4], dp[4];
@@ -309,10 +334,18 @@ __global__ __launch_bounds__(BW_THREADS, 1) void bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
             for (int db = 0; db < D_QK / 16; ++db) dk[db] = mfma16(bw_tr_a(qs_, BW_QROW, 32 * i, 16 * db, r, g), sb, dk[db]);
         }
-        // the next step's tiles into the other buffer (its last reader was step
-        // it-1, which every wave finished before the previous barrier)
-        if (it + 1 < n_steps) stage(buf ^ 1);
-        __syncthreads();
+        // step it+2 into the slot of step it-1, which every wave finished
+        // before the previous barrier; then step it+1 must have landed (only
+        // the copies just issued may stay in flight) before the bare barrier
+        if (it + 2 < n_steps) {
+            issue(it + 2);
+            __builtin_amdgcn_s_waitcnt(0x007D);   // vmcnt(13) lgkmcnt(0)
+        } else {
+            __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
+        }
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
     }
     // lane (r, g) holds dV[key r][16db + 4g + e] and dK[key r][16db + 4g + e] / scale
     if (key < T) {
@@ -330,12 +363,12 @@ __global__ __launch_bounds__(BW_THREADS, 1) void bwd_dkdv_kernel(BwdParams p) {
 
 // ---- 3. dQ.  Workgroup (KV head j, 64-query tile, sequence b); wave w owns
 // queries q0 + 16w .. +15.  Steps: (head, key block) over the 5 heads and the
-// key blocks the tile sees; the K and V tiles of the next step are copied while
-// the current one computes.  In C layout lane (r, g) holds element
+// key blocks the tile sees; the K and V tiles of a step are copied two steps
+// ahead into a ring of three LDS slots.  In C layout lane (r, g) holds element
 // [key 16kb + 4g + e][query r] of S^T, P^T, dP^T, dS^T.
 __global__ __launch_bounds__(BW_THREADS, 1) void bwd_dq_kernel(BwdParams p) {
-    __shared__ __attribute__((aligned(16))) __bf16 Ks[2][BW_T * BW_QROW];
-    __shared__ __attribute__((aligned(16))) __bf16 Vs[2][BW_T * BW_VROW];
+    __shared__ __attribute__((aligned(16))) __bf16 Ks[3][BW_T * BW_QROW];
+    __shared__ __attribute__((aligned(16))) __bf16 Vs[3][BW_T * BW_VROW];
     // longest first: the last query tiles see the most key blocks
     const int j = blockIdx.x, q0 = (gridDim.y - 1 - blockIdx.y) * BW_T, b = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, r = lane & 15, g = lane >> 4;
@@ -349,20 +382,28 @@ __global__ __launch_bounds__(BW_THREADS, 1) void bwd_dq_kernel(BwdParams p) {
     const __bf16 *kseq = p.k + ((long)b * T * p.n_kv + j) * D_QK;
     const __bf16 *vseq = p.v + ((long)b * T * p.n_kv + j) * D_V;
     const long kv_qs = (long)p.n_kv * D_QK, kv_vs = (long)p.n_kv * D_V;
-    BwStage<D_QK, D_V> st;
-    auto fetch = [&](int it) {
-        const int k0 = (kb_lo + it % n_kb) * BW_T;
-        st.load(kseq + (long)k0 * kv_qs, kv_qs, vseq + (long)k0 * kv_vs, kv_vs, min(BW_T, T - k0));
+    BwTileCopy<D_QK, BW_QROW> ck;
+    BwTileCopy<D_V, BW_VROW> cv;
+    ck.init(lane);
+    cv.init(lane);
+    const int uwave = __builtin_amdgcn_readfirstlane(wave);
+    // the copies of step it (key block kb_lo + it % n_kb) into slot it % 3
+    auto issue = [&](int it) {
+        const int slot = it % 3, k0 = (kb_lo + it % n_kb) * BW_T, n_valid = min(BW_T, T - k0);
+        const uint32_t krb = (uint32_t)kv_qs * 2, vrb = (uint32_t)kv_vs * 2;
+        ck.issue(bw_rsrc(kseq + (long)k0 * kv_qs, (uint32_t)n_valid * krb), krb, bw_lds(Ks[slot]), uwave);
+        cv.issue(bw_rsrc(vseq + (long)k0 * kv_vs, (uint32_t)n_valid * vrb), vrb, bw_lds(Vs[slot]), uwave);
     };
-    fetch(0);
-    st.store(Ks[0], BW_QROW, Vs[0], BW_VROW);
+    issue(0);
+    if (n_steps > 1) issue(1);
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
     __syncthreads();
 
     bf16x8 qf[D_QK / 32], hf[D_V / 32];
     float lse = 0.f, dl = 0.f;
     f32x4 dq[D_QK / 16];
     for (int it = 0; it < n_steps; ++it) {
-        const int h = it / n_kb, buf = it & 1, k0 = (kb_lo + it % n_kb) * BW_T;
+        const int h = it / n_kb, buf = it % 3, k0 = (kb_lo + it % n_kb) * BW_T;
         const BwHead hd = bw_head(p, b, j, h);
         if (it % n_kb == 0) {
             // a new head: its B operands Q_w^T and dH_w^T (lane: row q, values
@@ -381,7 +422,6 @@ __global__ __launch_bounds__(BW_THREADS, 1) void bwd_dq_kernel(BwdParams p) {
 #pragma unroll
             for (int i = 0; i < D_QK / 16; ++i) dq[i] = zero4;
         }
-        if (it + 1 < n_steps) fetch(it + 1);
         const __bf16 *ks_ = Ks[buf], *vs_ = Vs[buf];
         uint32_t sw[4][2];
 #pragma unroll
@@ -424,8 +464,17 @@ __global__ __launch_bounds__(BW_THREADS, 1) void bwd_dq_kernel(BwdParams p) {
                     u32x2{pack_bf16x2(dq[db][0] * p.scale, dq[db][1] * p.scale),
                           pack_bf16x2(dq[db][2] * p.scale, dq[db][3] * p.scale)};
         }
-        if (it + 1 < n_steps) st.store(Ks[buf ^ 1], BW_QROW, Vs[buf ^ 1], BW_VROW);
-        __syncthreads();
+        // step it+2 into the slot of step it-1 (finished by every wave before
+        // the previous barrier); step it+1 must have landed before the barrier
+        if (it + 2 < n_steps) {
+            issue(it + 2);
+            __builtin_amdgcn_s_waitcnt(0x007D);   // vmcnt(13) lgkmcnt(0)
+        } else {
+            __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
+        }
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
     }
 }
 
