@@ -235,12 +235,8 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_kernel(PrefillParams p)
 #pragma unroll
         for (int kk = 0; kk < KK_STEPS; ++kk) {
 #pragma unroll
-            for (int h = 0; h < GROUP; ++h) {
-                u32x4 w = ok ? ldg16(qsrow + h * D_QK + 32 * kk) : u32x4{0, 0, 0, 0};
-                qf[h][kk] = __builtin_bit_cast(bf16x8, w);
-            }
-            u32x4 w = ok ? ldg16(qnrow + 32 * kk) : u32x4{0, 0, 0, 0};
-            qf[GROUP][kk] = __builtin_bit_cast(bf16x8, w);
+            for (int h = 0; h < GROUP; ++h) qf[h][kk] = __builtin_bit_cast(bf16x8, ldg16(qsrow + h * D_QK + 32 * kk));
+            qf[GROUP][kk] = __builtin_bit_cast(bf16x8, ldg16(qnrow + 32 * kk));
         }
     };
     load_q(qt_first, qseq0, j);
@@ -271,15 +267,13 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_kernel(PrefillParams p)
     // visible keys of the row's own 16-key block (key tq is always visible).
     // K rows tw .. tw+15 come straight from global memory as A fragments.
     auto ref_pass = [&]() {
+        // (rows past the sequence end read row 0: their keys are visible only
+        // to rows past the end, which are never stored)
         const int key = tw + r;
-        const bool ok = key < T;
-        const __bf16 *krow = p.k + ((kseq0 + (ok ? key : 0)) * n_kv + j) * D_QK + 8 * g;
+        const __bf16 *krow = p.k + ((kseq0 + (key < T ? key : 0)) * n_kv + j) * D_QK + 8 * g;
         bf16x8 kf[KK_STEPS];
 #pragma unroll
-        for (int kk = 0; kk < KK_STEPS; ++kk) {
-            const u32x4 w = ok ? ldg16(krow + 32 * kk) : u32x4{0, 0, 0, 0};
-            kf[kk] = __builtin_bit_cast(bf16x8, w);
-        }
+        for (int kk = 0; kk < KK_STEPS; ++kk) kf[kk] = __builtin_bit_cast(bf16x8, ldg16(krow + 32 * kk));
         f32x4 bias[2];
         make_bias(tw, bias);          // block 0 of a slice starting at key tw
         f32x4 sd[HEADS];
