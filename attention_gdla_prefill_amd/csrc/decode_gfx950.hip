@@ -127,13 +127,12 @@ __global__ __launch_bounds__(DC_THREADS) void decode_split_kernel(DecodeParams p
         bf16x8 ka[2][D_QK / 32];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-            const int key = kb0 + 16 * kb + r;
+            // keys past the chunk read its last key (their scores are masked
+            // below and their weights are 0), so the loads need no branch
+            const int key = min(kb0 + 16 * kb + r, k_end - 1);
             const __bf16 *src = kbase + (long)key * krow + 8 * g;
 #pragma unroll
-            for (int kk = 0; kk < D_QK / 32; ++kk) {
-                u32x4 w = key < k_end ? ldg16(src + 32 * kk) : u32x4{0, 0, 0, 0};
-                ka[kb][kk] = __builtin_bit_cast(bf16x8, w);
-            }
+            for (int kk = 0; kk < D_QK / 32; ++kk) ka[kb][kk] = __builtin_bit_cast(bf16x8, ldg16(src + 32 * kk));
         }
         // V block: each lane takes 2 units of 4 keys x 8 columns
         u32x4 vr[2][4];
@@ -142,8 +141,8 @@ __global__ __launch_bounds__(DC_THREADS) void decode_split_kernel(DecodeParams p
             const int kg = (lane >> 4) + 4 * i, cc = lane & 15;
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) {
-                const int key = kb0 + 4 * kg + rr;
-                vr[i][rr] = key < k_end ? ldg16(vbase + (long)key * vrow + 8 * cc) : u32x4{0, 0, 0, 0};
+                const int key = min(kb0 + 4 * kg + rr, k_end - 1);
+                vr[i][rr] = ldg16(vbase + (long)key * vrow + 8 * cc);
             }
         }
 
