@@ -77,6 +77,29 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, ui
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, 0x00020000);
 }
 
+// This lane's index, read afresh: values derived from it are formed where they
+// are used rather than held in registers across the key loop.
+__device__ __forceinline__ int lane_now() {
+    int l;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+    return l;
+}
+// Buffer reads and writes at a byte offset: an offset at or past the
+// resource's size reads zeros and drops the write.  The query, gate, lambda
+// and output resources start at the first valid row of a query tile, so a row
+// before it has a negative offset (far past the size as unsigned; a lane's
+// column offset stays within its row, so the sum never wraps) and a row past
+// the last valid one lies past the size.
+__device__ __forceinline__ u32x4 bld16(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
+}
+__device__ __forceinline__ u32x2 bld8(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, 0);
+}
+__device__ __forceinline__ void bst8(__amdgpu_buffer_rsrc_t rs, uint32_t off, u32x2 v) {
+    __builtin_amdgcn_raw_buffer_store_b64(v, rs, off, 0, 0);
+}
+
 // One 16-byte buffer -> LDS copy per lane; lane l writes lds_base + 16*l.
 __device__ __forceinline__ void copy16_to_lds(__amdgpu_buffer_rsrc_t rsrc, uint32_t byte_off, __bf16 *lds_base) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t *)lds_base, 16, byte_off, 0, 0, 0);
@@ -226,17 +249,24 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_kernel(PrefillParams p)
     bf16x8 qf[HEADS][KK_STEPS];
     // B operand fragments of query tile qt of the sequence whose query rows
     // start at s0, KV head jj: lane holds Q[tq][32kk + 8g .. +7]
+    // Rows of the tile outside P .. T-1 read zeros (outside the resources), and
+    // qt < 0 (no next tile) reads nothing: the loads are issued unconditionally.
     auto load_q = [&](int qt, long s0, int jj) {
-        const int t = q0 + qt * PF_BM + 16 * wave + r;       // position
-        const bool ok = (!PREFIX || t >= P) && t < T;
-        const int qrow = ok ? (PREFIX ? t - P : t) : 0;
-        const __bf16 *qsrow = p.qs + ((s0 + qrow) * n_sig + GROUP * jj) * D_QK + 8 * g;
-        const __bf16 *qnrow = p.qn + ((s0 + qrow) * n_kv + jj) * D_QK + 8 * g;
+        const int tf = q0 + qt * PF_BM;                       // position of the tile's first row
+        const int lo = PREFIX ? max(tf, P) : tf, end = min(tf + PF_BM, T);
+        const long r0 = s0 + (PREFIX ? lo - P : lo);          // query row of position lo
+        const int ln = lane_now();
+        const int dt = tf + 16 * uwave + (ln & 15) - lo;      // row of this lane from the first valid one
+        const uint32_t nrows = qt < 0 ? 0u : (uint32_t)max(0, end - lo);
+        const auto qs_rs = make_rsrc(p.qs + (r0 * n_sig + GROUP * jj) * D_QK, nrows * (uint32_t)(n_sig * D_QK * 2));
+        const auto qn_rs = make_rsrc(p.qn + (r0 * n_kv + jj) * D_QK, nrows * (uint32_t)(n_kv * D_QK * 2));
+        const uint32_t os = (uint32_t)dt * (uint32_t)(n_sig * D_QK * 2) + 16 * (ln >> 4);
+        const uint32_t on = (uint32_t)dt * (uint32_t)(n_kv * D_QK * 2) + 16 * (ln >> 4);
 #pragma unroll
         for (int kk = 0; kk < KK_STEPS; ++kk) {
 #pragma unroll
-            for (int h = 0; h < GROUP; ++h) qf[h][kk] = __builtin_bit_cast(bf16x8, ldg16(qsrow + h * D_QK + 32 * kk));
-            qf[GROUP][kk] = __builtin_bit_cast(bf16x8, ldg16(qnrow + 32 * kk));
+            for (int h = 0; h < GROUP; ++h) qf[h][kk] = __builtin_bit_cast(bf16x8, bld16(qs_rs, os + h * D_QK * 2 + 64 * kk));
+            qf[GROUP][kk] = __builtin_bit_cast(bf16x8, bld16(qn_rs, on + 64 * kk));
         }
     };
     load_q(qt_first, qseq0, j);
@@ -267,13 +297,13 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_kernel(PrefillParams p)
     // visible keys of the row's own 16-key block (key tq is always visible).
     // K rows tw .. tw+15 come straight from global memory as A fragments.
     auto ref_pass = [&]() {
-        // (rows past the sequence end read row 0: their keys are visible only
+        // (rows past the sequence end read zeros: their keys are visible only
         // to rows past the end, which are never stored)
-        const int key = tw + r;
-        const __bf16 *krow = p.k + ((kseq0 + (key < T ? key : 0)) * n_kv + j) * D_QK + 8 * g;
+        const int ln = lane_now();
+        const uint32_t koff = (uint32_t)(tw + (ln & 15)) * krow_b + 16 * (ln >> 4);
         bf16x8 kf[KK_STEPS];
 #pragma unroll
-        for (int kk = 0; kk < KK_STEPS; ++kk) kf[kk] = __builtin_bit_cast(bf16x8, ldg16(krow + 32 * kk));
+        for (int kk = 0; kk < KK_STEPS; ++kk) kf[kk] = __builtin_bit_cast(bf16x8, bld16(k_rsrc, koff + 64 * kk));
         f32x4 bias[2];
         make_bias(tw, bias);          // block 0 of a slice starting at key tw
         f32x4 sd[HEADS];
@@ -467,19 +497,14 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_kernel(PrefillParams p)
         }
         ++n_done;
 
-        // ---- epilogue: normalise, differential combine, gate, bf16 store.  The
-        // gate and lambda of this tile are requested first, then the next query
-        // tile's queries, so that the epilogue does not wait behind those.
+        // ---- epilogue: normalise, differential combine, gate, bf16 store.
+        // Requested in this order: the first K/V tiles of what comes next, this
+        // tile's gate and lambda, the next query tile's queries; then the math
+        // and the stores.  No load or store depends on a branch, so the waits
+        // the compiler places are exact (no spill reload or untaken path forces
+        // a full drain).
         const bool row_ok = (!PREFIX || tq >= P) && tq < T;
-        const long row = qseq0 + (row_ok ? (PREFIX ? tq - P : tq) : 0);
-        u32x2 gw[GROUP][D_V / 16];
-#pragma unroll
-        for (int cb = 0; cb < D_V / 16; ++cb)
-#pragma unroll
-            for (int h = 0; h < GROUP; ++h)
-                gw[h][cb] = *reinterpret_cast<const u32x2 *>(p.gate + (row * n_sig + GROUP * j + h) * D_V +
-                                                            16 * cb + 4 * g);
-        const u32x2 lw = *reinterpret_cast<const u32x2 *>(p.lam + row * n_sig + GROUP * j);
+        const long row = qseq0 + (row_ok ? (PREFIX ? tq - P : tq) : 0);     // saved outputs only
         // next query tile of the run, or the first of the next work item: every
         // wave is done with the ring, so that item's first K/V tiles are copied
         // now, behind this epilogue, as are its queries
@@ -496,12 +521,36 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_kernel(PrefillParams p)
                 n_qt = -1;
             }
         }
-        if (n_qt >= 0) load_q(n_qt, (long)n_b * Tq, n_j);
+        // This tile's gate and lambda are requested after those copies and
+        // before the queries, so that their first use waits for them alone.
+        // Gate, lambda and out go through resources over the tile's valid rows:
+        // the other rows read zeros and their writes are dropped, so the loads
+        // and stores carry no branch.
+        const int e_lo = PREFIX ? max(t0, P) : t0, e_hi = min(t0 + PF_BM, T);
+        const long e_r0 = qseq0 + (PREFIX ? e_lo - P : e_lo);
+        const uint32_t e_rows = (uint32_t)max(0, e_hi - e_lo);
+        const auto g_rs = make_rsrc(p.gate + (e_r0 * n_sig + GROUP * j) * D_V, e_rows * (uint32_t)(n_sig * D_V * 2));
+        const auto o_rs = make_rsrc(p.out + (e_r0 * n_sig + GROUP * j) * D_V, e_rows * (uint32_t)(n_sig * D_V * 2));
+        const auto l_rs = make_rsrc(p.lam + e_r0 * n_sig + GROUP * j, e_rows * (uint32_t)(n_sig * 2));
+        const int eln = lane_now();
+        const int edt = tw + (eln & 15) - e_lo;               // row of this lane from the first valid one
+        const uint32_t e_off = (uint32_t)edt * (uint32_t)(n_sig * D_V * 2) + 8 * (eln >> 4);
+        u32x2 gw[GROUP][D_V / 16];
+#pragma unroll
+        for (int cb = 0; cb < D_V / 16; ++cb)
+#pragma unroll
+            for (int h = 0; h < GROUP; ++h) gw[h][cb] = bld8(g_rs, e_off + h * D_V * 2 + 32 * cb);
+        const u32x2 lw = bld8(l_rs, (uint32_t)edt * (uint32_t)(n_sig * 2));
+        load_q(n_qt, (long)n_b * Tq, n_j);
+        // (an opaque copy: the store offsets are then formed next to the
+        // stores, as immediates on one register)
+        uint32_t so = e_off;
+        asm volatile("" : "+v"(so));
 
         float inv[HEADS];
 #pragma unroll
         for (int h = 0; h < HEADS; ++h) inv[h] = 1.f / group4_sum(l_part[h]);
-        if (row_ok) {
+        {
             const float lam[GROUP] = {bf16_lo(lw[0]), bf16_hi(lw[0]), bf16_lo(lw[1]), bf16_hi(lw[1])};
 #pragma unroll
             for (int cb = 0; cb < D_V / 16; ++cb) {
@@ -521,18 +570,17 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_kernel(PrefillParams p)
                         const float hs = o[h][cb][e] * inv[h];
                         y[e] = gv[e] * fmaf(-lam[h], hn[e], hs);
                     }
-                    *reinterpret_cast<u32x2 *>(p.out + (row * n_sig + GROUP * j + h) * D_V + c) =
-                        u32x2{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
-                    if constexpr (TRAIN)
+                    bst8(o_rs, so + h * D_V * 2 + 32 * cb, u32x2{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])});
+                    if constexpr (TRAIN) if (row_ok)
                         *reinterpret_cast<u32x2 *>(p.hs + (row * n_sig + GROUP * j + h) * D_V + c) =
                             u32x2{pack_bf16x2(o[h][cb][0] * inv[h], o[h][cb][1] * inv[h]),
                                   pack_bf16x2(o[h][cb][2] * inv[h], o[h][cb][3] * inv[h])};
                 }
-                if constexpr (TRAIN)
+                if constexpr (TRAIN) if (row_ok)
                     *reinterpret_cast<u32x2 *>(p.hn + (row * n_kv + j) * D_V + c) =
                         u32x2{pack_bf16x2(hn[0], hn[1]), pack_bf16x2(hn[2], hn[3])};
             }
-            if constexpr (TRAIN) {
+            if constexpr (TRAIN) if (row_ok) {
                 // the weights were exp2(score * scale * log2(e) - m_ref) with sum 1/inv
                 if (g == 0) {
 #pragma unroll
@@ -555,9 +603,15 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_kernel(PrefillParams p)
     if (!more_items) break;
     ++round;
     qt_end = min(qt_first + p.run_len, p.n_qt);
-    // the next item's first tiles and queries have landed in every wave
-    wait_vmem();
-    __syncthreads();
+    // the next item's first tiles and queries have landed in every wave.
+    // Without the saved outputs a wave's last 32 memory operations are the
+    // output stores, which need not complete first: vmcnt(32).  The barrier is
+    // the bare s_barrier (a workgroup fence would wait for the stores too).
+    if constexpr (TRAIN) wait_vmem();
+    else __builtin_amdgcn_s_waitcnt(0x8F70);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
     }
 }
 
