@@ -96,8 +96,8 @@ __device__ __forceinline__ u32x4 bld16(__amdgpu_buffer_rsrc_t rs, uint32_t off) 
 __device__ __forceinline__ u32x2 bld8(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
     return __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, 0);
 }
-__device__ __forceinline__ void bst8(__amdgpu_buffer_rsrc_t rs, uint32_t off, u32x2 v) {
-    __builtin_amdgcn_raw_buffer_store_b64(v, rs, off, 0, 0);
+__device__ __forceinline__ void bst16(__amdgpu_buffer_rsrc_t rs, uint32_t off, u32x4 v) {
+    __builtin_amdgcn_raw_buffer_store_b128(v, rs, off, 0, 0);
 }
 
 // One 16-byte buffer -> LDS copy per lane; lane l writes lds_base + 16*l.
@@ -363,14 +363,18 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_kernel(PrefillParams p)
 #pragma unroll
             for (int i = 0; i < 4; ++i) l_part[h] = sum_bf16x2(pw[h][i], l_part[h]);
         }
-        // O^T += V^T P^T.  The A operand (16 columns c x 32 keys) comes from
-        // two transposing reads of row-major V: lane (r, g) receives
-        // V[4g + e][16cb + r] and V[16 + 4g + e][16cb + r], e = 0..3 -- the
-        // keys its P^T fragment holds in k-slots 8g..8g+7.
-        const __bf16 *vrd = vs + (32 * sub + 4 * g + (r >> 2)) * VS_ROW + 4 * (r & 3);
+        // O^T += V^T P^T.  The A operand (16 columns x 32 keys) comes from two
+        // transposing reads of row-major V: lane (r, g) receives V[4g + e][col]
+        // and V[16 + 4g + e][col], e = 0..3 -- the keys its P^T fragment holds
+        // in k-slots 8g..8g+7 -- for column col = 32c + 8(r/4) + 4s + r%4 of
+        // block cb = 2c + s.  With that order the output lane (r, g) holds
+        // columns 32c + 8g .. 32c + 8g + 7 of blocks 2c and 2c+1: 16 contiguous
+        // bytes for the gate loads and output stores.
+        const __bf16 *vrd = vs + (32 * sub + 4 * g + (r >> 2)) * VS_ROW + 8 * (r & 3);
         auto vfrag = [&](int cb) {
-            const s16x4 lo = lds_read_tr16(vrd + 16 * cb);
-            const s16x4 hi4 = lds_read_tr16(vrd + 16 * VS_ROW + 16 * cb);
+            const int cc = 32 * (cb >> 1) + 4 * (cb & 1);
+            const s16x4 lo = lds_read_tr16(vrd + cc);
+            const s16x4 hi4 = lds_read_tr16(vrd + 16 * VS_ROW + cc);
             const s16x4 v8[2] = {lo, hi4};
             return __builtin_bit_cast(bf16x8, v8);
         };
@@ -534,12 +538,12 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_kernel(PrefillParams p)
         const auto l_rs = make_rsrc(p.lam + e_r0 * n_sig + GROUP * j, e_rows * (uint32_t)(n_sig * 2));
         const int eln = lane_now();
         const int edt = tw + (eln & 15) - e_lo;               // row of this lane from the first valid one
-        const uint32_t e_off = (uint32_t)edt * (uint32_t)(n_sig * D_V * 2) + 8 * (eln >> 4);
-        u32x2 gw[GROUP][D_V / 16];
+        const uint32_t e_off = (uint32_t)edt * (uint32_t)(n_sig * D_V * 2) + 16 * (eln >> 4);
+        u32x4 gw[GROUP][D_V / 32];
 #pragma unroll
-        for (int cb = 0; cb < D_V / 16; ++cb)
+        for (int c = 0; c < D_V / 32; ++c)
 #pragma unroll
-            for (int h = 0; h < GROUP; ++h) gw[h][cb] = bld8(g_rs, e_off + h * D_V * 2 + 32 * cb);
+            for (int h = 0; h < GROUP; ++h) gw[h][c] = bld16(g_rs, e_off + h * D_V * 2 + 64 * c);
         const u32x2 lw = bld8(l_rs, (uint32_t)edt * (uint32_t)(n_sig * 2));
         load_q(n_qt, (long)n_b * Tq, n_j);
         // (an opaque copy: the store offsets are then formed next to the
@@ -553,32 +557,36 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_kernel(PrefillParams p)
         {
             const float lam[GROUP] = {bf16_lo(lw[0]), bf16_hi(lw[0]), bf16_lo(lw[1]), bf16_hi(lw[1])};
 #pragma unroll
-            for (int cb = 0; cb < D_V / 16; ++cb) {
-                const int c = 16 * cb + 4 * g;
-                float hn[4];
+            for (int c = 0; c < D_V / 32; ++c) {
+                // columns 32c + 8g .. +7: blocks 2c (first four) and 2c + 1
+                const int col = 32 * c + 8 * g;
+                float hn[8];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) hn[e] = o[GROUP][cb][e] * inv[GROUP];
+                for (int e = 0; e < 8; ++e) hn[e] = o[GROUP][2 * c + e / 4][e % 4] * inv[GROUP];
 #pragma unroll
                 for (int h = 0; h < GROUP; ++h) {
-                    const float gv[4] = {bf16_lo(gw[h][cb][0]), bf16_hi(gw[h][cb][0]),
-                                         bf16_lo(gw[h][cb][1]), bf16_hi(gw[h][cb][1])};
-                    float y[4];
+                    float y[8], hs[8];
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
+                    for (int e = 0; e < 8; ++e) {
+                        const uint32_t gword = gw[h][c][e / 2];
+                        const float gv = (e & 1) ? bf16_hi(gword) : bf16_lo(gword);
                         // H_S and H_N are formed the same way, so identical queries with
                         // lambda = 1 give exactly 0
-                        const float hs = o[h][cb][e] * inv[h];
-                        y[e] = gv[e] * fmaf(-lam[h], hn[e], hs);
+                        hs[e] = o[h][2 * c + e / 4][e % 4] * inv[h];
+                        y[e] = gv * fmaf(-lam[h], hn[e], hs[e]);
                     }
-                    bst8(o_rs, so + h * D_V * 2 + 32 * cb, u32x2{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])});
+                    bst16(o_rs, so + h * D_V * 2 + 64 * c,
+                          u32x4{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]), pack_bf16x2(y[4], y[5]),
+                                pack_bf16x2(y[6], y[7])});
                     if constexpr (TRAIN) if (row_ok)
-                        *reinterpret_cast<u32x2 *>(p.hs + (row * n_sig + GROUP * j + h) * D_V + c) =
-                            u32x2{pack_bf16x2(o[h][cb][0] * inv[h], o[h][cb][1] * inv[h]),
-                                  pack_bf16x2(o[h][cb][2] * inv[h], o[h][cb][3] * inv[h])};
+                        *reinterpret_cast<u32x4 *>(p.hs + (row * n_sig + GROUP * j + h) * D_V + col) =
+                            u32x4{pack_bf16x2(hs[0], hs[1]), pack_bf16x2(hs[2], hs[3]), pack_bf16x2(hs[4], hs[5]),
+                                  pack_bf16x2(hs[6], hs[7])};
                 }
                 if constexpr (TRAIN) if (row_ok)
-                    *reinterpret_cast<u32x2 *>(p.hn + (row * n_kv + j) * D_V + c) =
-                        u32x2{pack_bf16x2(hn[0], hn[1]), pack_bf16x2(hn[2], hn[3])};
+                    *reinterpret_cast<u32x4 *>(p.hn + (row * n_kv + j) * D_V + col) =
+                        u32x4{pack_bf16x2(hn[0], hn[1]), pack_bf16x2(hn[2], hn[3]), pack_bf16x2(hn[4], hn[5]),
+                              pack_bf16x2(hn[6], hn[7])};
             }
             if constexpr (TRAIN) if (row_ok) {
                 // the weights were exp2(score * scale * log2(e) - m_ref) with sum 1/inv
