@@ -96,8 +96,12 @@ __device__ __forceinline__ u32x4 bld16(__amdgpu_buffer_rsrc_t rs, uint32_t off) 
 __device__ __forceinline__ u32x2 bld8(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
     return __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, 0);
 }
+// The output store is non-temporal (cache policy nt): the output is written
+// once and never read back here, and keeping it out of the caches' normal
+// replacement measured faster on full-causal layers (4K: 0.445 -> 0.437 ms)
+// and within 1 % on a 128-token window.
 __device__ __forceinline__ void bst16(__amdgpu_buffer_rsrc_t rs, uint32_t off, u32x4 v) {
-    __builtin_amdgcn_raw_buffer_store_b128(v, rs, off, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(v, rs, off, 0, 2);
 }
 
 // One 16-byte buffer -> LDS copy per lane; lane l writes lds_base + 16*l.
@@ -612,11 +616,12 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_kernel(PrefillParams p)
     ++round;
     qt_end = min(qt_first + p.run_len, p.n_qt);
     // the next item's first tiles and queries have landed in every wave.
-    // Without the saved outputs a wave's last 32 memory operations are the
-    // output stores, which need not complete first: vmcnt(32).  The barrier is
+    // Without the saved outputs a wave's last 16 memory operations are the
+    // output stores, which need not complete first: vmcnt(16).  The barrier is
     // the bare s_barrier (a workgroup fence would wait for the stores too).
+    static_assert(GROUP * D_V / 32 == 16, "output stores per wave");
     if constexpr (TRAIN) wait_vmem();
-    else __builtin_amdgcn_s_waitcnt(0x8F70);
+    else __builtin_amdgcn_s_waitcnt(0x4F70);
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
