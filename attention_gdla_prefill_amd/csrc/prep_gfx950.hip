@@ -45,6 +45,7 @@ struct PrepParams {
 constexpr int PP_GATE_PARTS = 4;
 constexpr int PP_JOBS = 2 + PP_GATE_PARTS;
 constexpr int PP_HB = 4;              // head blocks of 16 per lambda pass (64 heads)
+constexpr int PP_BATCH = 4;           // rotary tasks / gate chunks per thread in flight
 
 __device__ __forceinline__ uint32_t rotate_pair(uint32_t w, float2 c) {
     const float x0 = bf16_lo(w), x1 = bf16_hi(w);
@@ -126,16 +127,34 @@ __global__ __launch_bounds__(PP_THREADS) void prep_kernel(PrepParams p) {
         __syncthreads();
         // ---- rotary parts of the query heads, in place: a task is one 16-byte
         // chunk (4 pairs) of one head of one token; 8 chunks per head
+        // PP_BATCH tasks per thread are loaded before any is stored (the
+        // compiler cannot move a load above a store that may alias it), so
+        // their memory latencies overlap; a task past the end re-reads the last
+        // task's chunk and is not stored.
         const int n_tasks = n_tok_blk * n_qh * 8;
-        for (int i = tid; i < n_tasks; i += PP_THREADS) {
-            const int tl = i / (n_qh * 8), rem = i % (n_qh * 8), h = rem / 8, ch = rem % 8;
-            const long tok = tok0 + tl;
-            __bf16 *row = h < n_sig ? p.qs + (tok * n_sig + h) * D_QK : p.qn + (tok * p.n_kv + (h - n_sig)) * D_QK;
-            u32x4 *src = reinterpret_cast<u32x4 *>(row + (D_QK - PP_ROT) + 8 * ch);
-            u32x4 w = *src;
+        for (int i0 = tid; i0 < n_tasks; i0 += PP_BATCH * PP_THREADS) {
+            u32x4 *addr[PP_BATCH];
+            u32x4 w[PP_BATCH];
+            int tls[PP_BATCH], chs[PP_BATCH];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) w[e] = rotate_pair(w[e], cs[tl][4 * ch + e]);
-            *src = w;
+            for (int u = 0; u < PP_BATCH; ++u) {
+                const int i = min(i0 + u * PP_THREADS, n_tasks - 1);
+                const int tl = i / (n_qh * 8), rem = i % (n_qh * 8), h = rem / 8, ch = rem % 8;
+                const long tok = tok0 + tl;
+                __bf16 *row = h < n_sig ? p.qs + (tok * n_sig + h) * D_QK
+                                        : p.qn + (tok * p.n_kv + (h - n_sig)) * D_QK;
+                addr[u] = reinterpret_cast<u32x4 *>(row + (D_QK - PP_ROT) + 8 * ch);
+                tls[u] = tl;
+                chs[u] = ch;
+                w[u] = *addr[u];
+            }
+#pragma unroll
+            for (int u = 0; u < PP_BATCH; ++u) {
+                if (i0 + u * PP_THREADS >= n_tasks) break;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) w[u][e] = rotate_pair(w[u][e], cs[tls[u]][4 * chs[u] + e]);
+                *addr[u] = w[u];
+            }
         }
         // ---- the shared rotary key: rotated once per chunk, written to every KV head
         for (int i = tid; i < n_tok_blk * 8; i += PP_THREADS) {
@@ -156,14 +175,21 @@ __global__ __launch_bounds__(PP_THREADS) void prep_kernel(PrepParams p) {
         const long hi = tok0 * per_tok + n_chunks * (part + 1) / PP_GATE_PARTS;
         const u32x4 *src = reinterpret_cast<const u32x4 *>(p.gate_pre);
         u32x4 *dst = reinterpret_cast<u32x4 *>(p.gate);
-        for (long c = lo + tid; c < hi; c += PP_THREADS) {
-            u32x4 w = src[c];
+        // PP_BATCH chunks per thread in flight (loads first, as above)
+        for (long c0 = lo + tid; c0 < hi; c0 += PP_BATCH * PP_THREADS) {
+            u32x4 w[PP_BATCH];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float z0 = bf16_lo(w[e]), z1 = bf16_hi(w[e]);
-                w[e] = pack_bf16x2(1.f / (1.f + __expf(-z0)), 1.f / (1.f + __expf(-z1)));
+            for (int u = 0; u < PP_BATCH; ++u) w[u] = src[min(c0 + (long)u * PP_THREADS, hi - 1)];
+#pragma unroll
+            for (int u = 0; u < PP_BATCH; ++u) {
+                if (c0 + (long)u * PP_THREADS >= hi) break;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float z0 = bf16_lo(w[u][e]), z1 = bf16_hi(w[u][e]);
+                    w[u][e] = pack_bf16x2(1.f / (1.f + __expf(-z0)), 1.f / (1.f + __expf(-z1)));
+                }
+                dst[c0 + (long)u * PP_THREADS] = w[u];
             }
-            dst[c] = w;
         }
     }
 }
