@@ -117,6 +117,38 @@ def test_prefill_window_ge_T_equals_full():
     assert torch.equal(gpu_prefill(x, 0), gpu_prefill(x, 200))
 
 
+GUARD_CASES = [
+    # (B, P, T_q, n_kv, window): ragged sequence ends, one row, unaligned prefixes
+    (2, 0, 100, 2, 0), (1, 0, 37, 1, 64), (2, 0, 1, 2, 0), (2, 100, 37, 3, 0), (1, 127, 129, 2, 128),
+]
+
+
+@pytest.mark.parametrize("case", GUARD_CASES, ids=lambda c: "B%d_P%d_Tq%d_kv%d_W%d" % c)
+def test_prefill_writes_only_its_rows(case):
+    """Rows of a 64-row query tile outside the sequence (past its end, or
+    before the first query of a prefix call) are computed but their stores are
+    dropped: 64 rows of guard on each side of the output keep their value, and
+    the output matches the oracle."""
+    import attention_gdla_prefill_amd as gdla
+    B, P, Tq, n_kv, window = case
+    log("prefill guard rows %s" % (case,))
+    x = to_dev(W.prefill_inputs(small(B, P + Tq, n_kv), seed=90 + P + Tq, **SHARP))
+    n_sig = 4 * n_kv
+    guard, n = 64 * n_sig * 128, B * Tq * n_sig * 128
+    big = torch.full((n + 2 * guard,), 1234.0, dtype=torch.bfloat16, device="cuda")
+    out = big[guard:guard + n].view(B, Tq, n_sig, 128)
+    out.fill_(float("nan"))
+    y = query_tail(x, P)
+    call = gdla.prefill_prefix if P else gdla.prefill
+    call(y["q_signal"], y["q_noise"], y["k"], y["v"], y["lam"], y["gate"], window=window, out=out)
+    torch.cuda.synchronize()
+    assert bool((big[:guard] == 1234.0).all()) and bool((big[guard + n:] == 1234.0).all())
+    rb = np.repeat(np.arange(B, dtype=np.int32), Tq)
+    rt = np.tile(np.arange(P, P + Tq, dtype=np.int32), B)
+    want = oracle_prefill_rows(x, window, rb, rt).reshape(B, Tq, n_sig, 128)
+    compare(out, want, "guard rows P=%d Tq=%d W=%d" % (P, Tq, window))
+
+
 def test_prefill_rejects_bad_tensors():
     import attention_gdla_prefill_amd as gdla
     x = to_dev(W.prefill_inputs(small(1, 32, 1), seed=9))
