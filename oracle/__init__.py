@@ -5,7 +5,8 @@ Only the tests, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 ``attention_gdla_prefill_amd`` never imports it, and the two share no code.
 
 The arithmetic lives in ``gdla_oracle.c`` (plain C, fp64 sums and exponentials,
-two-pass softmax).  This module only marshals numpy arrays into it:
+two-pass softmax; :func:`library_fp32` loads the same source built with fp32
+arithmetic).  This module only marshals numpy arrays into it:
 
 * :func:`prefill` -- every query position of a [B, T] prefill;
 * :func:`prefill_rows` -- a chosen list of (b, t) positions, for workloads too
@@ -56,6 +57,8 @@ def _bind(path):
         _f64p, _f64p, _f64p, _f64p, _f64p]
     lib.gdla_oracle_num_threads.restype = ctypes.c_int
     lib.gdla_oracle_num_threads.argtypes = []
+    lib.gdla_oracle_set_threads.restype = None
+    lib.gdla_oracle_set_threads.argtypes = [ctypes.c_int]
     return lib
 
 
@@ -71,9 +74,29 @@ def library(path=None):
     return _LIB
 
 
-def num_threads():
+_LIB_FP32 = None
+
+
+def library_fp32():
+    """The fp32 build of the same source (built with gcc on first use if
+    missing): every prefill and decode product, sum and exponential in fp32."""
+    global _LIB_FP32
+    if _LIB_FP32 is None:
+        if not os.path.exists(_build.LIBRARY_FP32):
+            _build.build_oracle(fp32=True)
+        _LIB_FP32 = _bind(_build.LIBRARY_FP32)
+    return _LIB_FP32
+
+
+def num_threads(lib=None):
     """OpenMP threads the oracle's parallel loops use on this host."""
-    return int(library().gdla_oracle_num_threads())
+    return int((lib or library()).gdla_oracle_num_threads())
+
+
+def set_threads(n, lib=None):
+    """Threads for the oracle's later parallel loops (the build's own OpenMP
+    runtime; n >= 1)."""
+    (lib or library()).gdla_oracle_set_threads(int(n))
 
 
 def _f32(a):

@@ -53,7 +53,66 @@
 #define ORACLE_MUTANT 0
 #endif
 
+/*
+ * Arithmetic type of the prefill and decode definitions.  The normal build
+ * carries every product, sum and exponential in fp64.  Built with
+ * -DORACLE_FP32, the same source carries them in fp32 (exp becomes expf):
+ * the plain fp32 CPU reference whose speed is reported beside the GPU's.
+ * The latent decode and the pre-attention step are always fp64.
+ */
+#ifdef ORACLE_FP32
+typedef float real;
+#define EXP expf
+#else
+typedef double real;
+#define EXP exp
+#endif
+
+/* Largest query-key head dim the prefill and decode definitions accept. */
+#define ORACLE_MAX_DQK 1024
+
 enum { ORACLE_OK = 0, ORACLE_BAD_ARG = 1, ORACLE_NO_MEMORY = 2 };
+
+/*
+ * Scores of one query vector q[d_qk] against the keys s_lo..s_hi-1 of one KV
+ * head:  z[s - s_lo] = scale * sum_d q[d] k_s[d].  Each dot product is summed
+ * over d in ascending order; eight keys are taken at a time only so that
+ * their (independent) sums overlap in the CPU's pipeline.
+ */
+static void scores(const real *q, const float *k, long k_stride, long s_lo, long s_hi,
+                   int d_qk, real scale, real *z)
+{
+#if ORACLE_MUTANT == 5
+    const int d_end = d_qk - 64;                 /* planted: drops the 64-dim rotary tail */
+#else
+    const int d_end = d_qk;
+#endif
+    long s = s_lo;
+    for (; s + 8 <= s_hi; s += 8) {
+        const float *ks = k + s * k_stride;
+        real acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        for (int d = 0; d < d_end; ++d) {
+#pragma GCC unroll 8
+            for (int u = 0; u < 8; ++u)
+                acc[u] += q[d] * (real)ks[u * k_stride + d];
+        }
+        for (int u = 0; u < 8; ++u)
+            z[s + u - s_lo] = acc[u];
+    }
+    for (; s < s_hi; ++s) {
+        const float *ks = k + s * k_stride;
+        real dot = 0;
+        for (int d = 0; d < d_end; ++d)
+            dot += q[d] * (real)ks[d];
+        z[s - s_lo] = dot;
+    }
+    for (long i = 0; i < s_hi - s_lo; ++i)
+#if ORACLE_MUTANT == 6
+        (void)scale;                             /* planted: forgets the scale */
+#else
+        z[i] = scale * z[i];
+#endif
+}
 
 /*
  * Softmax attention of one query vector q[d_qk] over the keys s_lo..s_hi-1
@@ -61,40 +120,29 @@ enum { ORACLE_OK = 0, ORACLE_BAD_ARG = 1, ORACLE_NO_MEMORY = 2 };
  *   z_s = scale * sum_d q[d] k_s[d]
  *   out = sum_s exp(z_s - max z) v_s / sum_s exp(z_s - max z)
  * Key row s lives at k + s*k_stride, value row s at v + s*v_stride.
- * z is caller scratch of at least s_hi - s_lo doubles.
+ * z is caller scratch of at least s_hi - s_lo values.
  */
-static void attend_one(const float *q, const float *k, long k_stride,
+static void attend_one(const float *qf, const float *k, long k_stride,
                        const float *v, long v_stride, long s_lo, long s_hi,
-                       int d_qk, int d_v, double scale, double *z, double *out)
+                       int d_qk, int d_v, real scale, real *z, real *out)
 {
-    double zmax = -INFINITY;
-    for (long s = s_lo; s < s_hi; ++s) {
-        const float *ks = k + s * k_stride;
-        double dot = 0.0;
-#if ORACLE_MUTANT == 5
-        for (int d = 0; d + 64 < d_qk; ++d)      /* planted: drops the 64-dim rotary tail */
-#else
-        for (int d = 0; d < d_qk; ++d)
-#endif
-            dot += (double)q[d] * (double)ks[d];
-#if ORACLE_MUTANT == 6
-        z[s - s_lo] = dot;                       /* planted: forgets the scale */
-        (void)scale;
-#else
-        z[s - s_lo] = scale * dot;
-#endif
+    real q[ORACLE_MAX_DQK];
+    for (int d = 0; d < d_qk; ++d)
+        q[d] = (real)qf[d];
+    scores(q, k, k_stride, s_lo, s_hi, d_qk, scale, z);
+    real zmax = -INFINITY;
+    for (long s = s_lo; s < s_hi; ++s)
         if (z[s - s_lo] > zmax)
             zmax = z[s - s_lo];
-    }
-    double denom = 0.0;
+    real denom = 0;
     for (int c = 0; c < d_v; ++c)
-        out[c] = 0.0;
+        out[c] = 0;
     for (long s = s_lo; s < s_hi; ++s) {
-        double e = exp(z[s - s_lo] - zmax);
+        const real e = EXP(z[s - s_lo] - zmax);
         denom += e;
         const float *vs = v + s * v_stride;
         for (int c = 0; c < d_v; ++c)
-            out[c] += e * (double)vs[c];
+            out[c] += e * (real)vs[c];
     }
     for (int c = 0; c < d_v; ++c)
         out[c] /= denom;
@@ -122,9 +170,9 @@ static long first_visible(long t, int window)
  */
 static void group_row(const float *qs, const float *qn_row, int j, int n_kv,
                       const float *k, long k_stride, const float *v, long v_stride,
-                      long s_lo, long s_hi, int group, int d_qk, int d_v, double scale,
-                      const float *lam, const float *gate, double *z,
-                      double *h_noise, double *h_sig, double *out)
+                      long s_lo, long s_hi, int group, int d_qk, int d_v, real scale,
+                      const float *lam, const float *gate, real *z,
+                      real *h_noise, real *h_sig, double *out)
 {
     attend_one(qn_row + (long)j * d_qk, k, k_stride, v, v_stride, s_lo, s_hi, d_qk, d_v,
                scale, z, h_noise);
@@ -140,15 +188,15 @@ static void group_row(const float *qs, const float *qn_row, int j, int n_kv,
                    d_qk, d_v, scale, z, h_sig);
         for (int c = 0; c < d_v; ++c) {
 #if ORACLE_MUTANT == 2
-            double d = h_sig[c] + (double)lam[i] * h_noise[c];   /* planted: wrong sign */
+            const real d = h_sig[c] + (real)lam[i] * h_noise[c];  /* planted: wrong sign */
 #else
-            double d = h_sig[c] - (double)lam[i] * h_noise[c];
+            const real d = h_sig[c] - (real)lam[i] * h_noise[c];
 #endif
 #if ORACLE_MUTANT == 4
             out[(long)i * d_v + c] = d;                          /* planted: gate not applied */
             (void)gate;
 #else
-            out[(long)i * d_v + c] = (double)gate[(long)i * d_v + c] * d;
+            out[(long)i * d_v + c] = (real)gate[(long)i * d_v + c] * d;
 #endif
         }
     }
@@ -156,7 +204,7 @@ static void group_row(const float *qs, const float *qn_row, int j, int n_kv,
 
 static int dims_ok(int n_kv, int group, int d_qk, int d_v)
 {
-    return n_kv >= 1 && group >= 1 && d_qk >= 1 && d_v >= 1;
+    return n_kv >= 1 && group >= 1 && d_qk >= 1 && d_qk <= ORACLE_MAX_DQK && d_v >= 1;
 }
 
 /*
@@ -195,9 +243,9 @@ int gdla_oracle_prefill_rows(const float *k, const float *v, int B, int T, int n
 
 #pragma omp parallel
     {
-        double *z = (double *)malloc(sizeof(double) * (size_t)T);
-        double *hn = (double *)malloc(sizeof(double) * (size_t)d_v);
-        double *hs = (double *)malloc(sizeof(double) * (size_t)d_v);
+        real *z = (real *)malloc(sizeof(real) * (size_t)T);
+        real *hn = (real *)malloc(sizeof(real) * (size_t)d_v);
+        real *hs = (real *)malloc(sizeof(real) * (size_t)d_v);
         if (!z || !hn || !hs) {
 #pragma omp atomic write
             failed = 1;
@@ -216,7 +264,7 @@ int gdla_oracle_prefill_rows(const float *k, const float *v, int B, int T, int n
                 group_row(q_signal + (r * n_sig + (long)j * group) * d_qk,
                           q_noise + r * n_kv * d_qk, j, n_kv,
                           kb, k_stride, vb, v_stride, first_visible(t, window), t + 1,
-                          group, d_qk, d_v, scale,
+                          group, d_qk, d_v, (real)scale,
                           lam + r * n_sig + (long)j * group,
                           gate + (r * n_sig + (long)j * group) * d_v, z, hn, hs,
                           out + (r * n_sig + (long)j * group) * d_v);
@@ -265,9 +313,9 @@ int gdla_oracle_decode(const float *q_signal, const float *q_noise, const float 
 
 #pragma omp parallel
     {
-        double *z = (double *)malloc(sizeof(double) * (size_t)max_len);
-        double *hn = (double *)malloc(sizeof(double) * (size_t)d_v);
-        double *hs = (double *)malloc(sizeof(double) * (size_t)d_v);
+        real *z = (real *)malloc(sizeof(real) * (size_t)max_len);
+        real *hn = (real *)malloc(sizeof(real) * (size_t)d_v);
+        real *hs = (real *)malloc(sizeof(real) * (size_t)d_v);
         if (!z || !hn || !hs) {
 #pragma omp atomic write
             failed = 1;
@@ -283,7 +331,7 @@ int gdla_oracle_decode(const float *q_signal, const float *q_noise, const float 
                 group_row(q_signal + (b * n_sig + (long)j * group) * d_qk,
                           q_noise + b * n_kv * d_qk, j, n_kv,
                           kb, k_stride, vb, v_stride, first_visible(t, window), t + 1,
-                          group, d_qk, d_v, scale,
+                          group, d_qk, d_v, (real)scale,
                           lam + b * n_sig + (long)j * group,
                           gate + (b * n_sig + (long)j * group) * d_v, z, hn, hs,
                           out + (b * n_sig + (long)j * group) * d_v);
@@ -540,6 +588,13 @@ int gdla_oracle_prep(const float *q_signal, const float *q_noise, const float *k
             gate_out[bt * n_sig * d_v + e] = sigmoid((double)gate_pre[bt * n_sig * d_v + e]);
     }
     return ORACLE_OK;
+}
+
+/* Threads for later parallel regions of this library (n >= 1). */
+void gdla_oracle_set_threads(int n)
+{
+    if (n >= 1)
+        omp_set_num_threads(n);
 }
 
 /* Number of OpenMP threads a parallel region of this library would use. */
