@@ -121,11 +121,6 @@ struct BwTileCopy {
     }
 };
 static_assert(64 / (BW_QROW / 8) == 2 && 64 / (BW_VROW / 8) == 3, "rows per copy");
-// copies one wave issues per step, at least: 8 of a 192-wide tile, 5 of a
-// 128-wide one; the wait at a step's end leaves this many (the next step's
-// copies, issued last) in flight
-constexpr int BW_STEP_COPIES_MIN = 13;
-
 __device__ __forceinline__ bool bw_visible(int q, int key, int T, int window) {
     return q < T && key <= q && (window == 0 || q - key < window);
 }

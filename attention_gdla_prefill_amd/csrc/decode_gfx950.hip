@@ -2,9 +2,12 @@
 //
 // Decode reads the whole visible KV cache of every (sequence, KV head) once
 // and does little arithmetic per byte, so it is bound by HBM bandwidth; the
-// KV cache is what grows with the context (the report's motivation for the
-// latent KV path: aitrends.kr GDLA paragraph; metalmedia P4 summary).  The
-// five query heads of a group (4 signal + 1 noise) share each K/V byte read.
+// KV cache is what grows with the context (idailynews, "연속기획⑩ 독자 AI 2차
+// 평가 Motif 3 모델과 인프라 함께 설계", section "GDLA로 긴 문맥과 메모리 부담
+// 함께 다뤄": the cache grows with the context and the sliding-window layers
+// cover 128 tokens; aitrends.kr, GDLA paragraph: the latent KV path exists to
+// shrink it).  The five query heads of a group (4 signal + 1 noise) share
+// each K/V byte read.
 //
 // Split-KV: workgroup (split s, KV head j, sequence b) covers one contiguous
 // chunk of the visible keys; its 4 waves take 32-key blocks of the chunk in
@@ -266,6 +269,217 @@ __global__ __launch_bounds__(D_V) void decode_combine_kernel(DecodeParams p) {
     decode_epilogue(p, b, j, c, load_gate_col(p, b, j, c), A, Ls);
 }
 
+// ---- window decode: every visible key of a (sequence, KV head) in one
+// workgroup, no partials ------------------------------------------------------
+//
+// A 128-key window (the report's sliding-window layers) makes each
+// (sequence, KV head) a short, independent job: 80 KB of K and V, five query
+// heads.  Its time is the latency of one pass over HBM, so the kernel issues
+// every load of the job at its start -- queries, K straight into matrix-core
+// operand registers, V straight into LDS (direct buffer -> LDS loads), the
+// gate and lambda -- and keeps LDS at 37 KB so that all (sequence, KV head)
+// workgroups of a 64-sequence batch are resident at once (four per CU).
+//   wave w: keys 32w .. 32w+31 of the window; S^T = K Q^T (12 MFMAs);
+//   the row maxima meet in LDS (one barrier), so every wave takes its weights
+//   against the same reference and nothing is rescaled;
+//   O^T += V^T P^T with V^T read by the transposing LDS read;
+//   the four partial sums meet in LDS (second barrier) and 64 threads apply
+//   the combine and the gate, 16 bytes each.
+constexpr int DW_KEYS = 128;                  // keys per workgroup: 4 waves x 32
+constexpr int DW_VCH = D_V / 8 + 2;           // 16-byte chunks per padded V row in LDS (32-byte pad)
+constexpr int DW_VROW = DW_VCH * 8;           // bf16 per padded V row
+constexpr int DW_VROWS_PER_COPY = 3;          // a copy instruction covers 3 rows (54 of 64 lanes)
+constexpr int DW_WAVE_COPIES = (32 + DW_VROWS_PER_COPY - 1) / DW_VROWS_PER_COPY;   // 11
+static_assert(DW_VROWS_PER_COPY * DW_VCH <= 64, "rows per copy");
+static_assert(HEADS * D_V * 4 <= 32 * DW_VROW * 2, "a wave's partial sums fit its V rows");
+
+typedef short dw_s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) dw_s16x4 dw_lds_s16x4_t;
+typedef __attribute__((address_space(3))) void dw_lds_void_t;
+
+// Buffer resource over `bytes` bytes from `base`: reads at or past the size
+// return zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t dw_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, 0x00020000);
+}
+
+__global__ __launch_bounds__(DC_THREADS) void decode_window_kernel(DecodeParams p) {
+    // V rows of the window, padded (the padding keeps the transposing reads of
+    // 16 consecutive rows free of bank conflicts); after its products, wave w
+    // reuses its own 32 rows for its partial sums
+    __shared__ __attribute__((aligned(16))) __bf16 Vs[DW_KEYS * DW_VROW];
+    __shared__ float red_m[DC_WAVES][16], red_l[DC_WAVES][16];
+
+    const int j = blockIdx.x, b = blockIdx.y;
+    const int n_kv = p.n_kv, n_sig = n_kv * GROUP;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int r = lane & 15, g = lane >> 4;
+    const int uwave = __builtin_amdgcn_readfirstlane(wave);
+
+    // ---- every load of the job, before any wait.  The sequence offsets are
+    // read first, as a vector load: the queries, the gate and lambda (which do
+    // not depend on them) follow at once, and the wait for the offsets is then
+    // a count of the loads behind them, not a full drain.
+    const auto cu_rs = dw_rsrc(p.cu, (gridDim.y + 1) * 4u);
+    const u32x2 cuv = __builtin_amdgcn_raw_buffer_load_b64(cu_rs, 4u * b, 0, 0);   // cu[b], cu[b+1]
+    // queries: column r of the B operand; r < 4 signal head 4j+r, r == 4 noise
+    // head j, the other columns read zeros (an empty resource)
+    bf16x8 qf[D_QK / 32];
+    {
+        // two resources, each uniform over the wave; a lane's offset lies past
+        // the one that does not hold its query, which then reads zeros
+        const auto qs_rs = dw_rsrc(p.qs + ((long)b * n_sig + GROUP * j) * D_QK, GROUP * D_QK * 2);
+        const auto qn_rs = dw_rsrc(p.qn + ((long)b * n_kv + j) * D_QK, D_QK * 2);
+        const uint32_t far = 1u << 30;
+        const uint32_t os = r < GROUP ? (uint32_t)r * D_QK * 2 + 16 * g : far;
+        const uint32_t on = r == GROUP ? 16u * g : far;
+#pragma unroll
+        for (int kk = 0; kk < D_QK / 32; ++kk) {
+            const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(qs_rs, os + 64 * kk, 0, 0);
+            const u32x4 n = __builtin_amdgcn_raw_buffer_load_b128(qn_rs, on + 64 * kk, 0, 0);
+            qf[kk] = __builtin_bit_cast(bf16x8, a | n);
+        }
+    }
+    // epilogue operands: thread t < 64 forms signal head 4j + t/16, columns
+    // 8(t%16) .. +7
+    // (wave 0 only: the other waves' resources are empty and read zeros, so
+    // the loads carry no branch and nothing waits for them before their use)
+    const int eh = (tid >> 4) & 3, ec = 8 * (tid & 15);
+    const long orow0 = (long)b * n_sig + GROUP * j;                 // signal head 4j
+    const auto g_rs = dw_rsrc(p.gate + orow0 * D_V, uwave == 0 ? GROUP * D_V * 2 : 0);
+    const auto l_rs = dw_rsrc(p.lam + orow0, uwave == 0 ? GROUP * 2 : 0);
+    const u32x4 gw = __builtin_amdgcn_raw_buffer_load_b128(g_rs, (uint32_t)(eh * D_V + ec) * 2, 0, 0);
+    const u32x2 lw = __builtin_amdgcn_raw_buffer_load_b64(l_rs, 0, 0, 0);   // lambda of the 4 signal heads
+
+    const int start = __builtin_amdgcn_readfirstlane((int)cuv[0]);
+    const int L = __builtin_amdgcn_readfirstlane((int)cuv[1]) - start;
+    const int vis_lo = max(0, L - p.window);
+    const int n_vis = max(0, L - vis_lo);          // <= DW_KEYS
+    const long row0 = (long)start + vis_lo;        // first visible cache row
+
+    const uint32_t krow_b = (uint32_t)n_kv * D_QK * 2, vrow_b = (uint32_t)n_kv * D_V * 2;
+    const auto k_rs = dw_rsrc(p.kc + (row0 * n_kv + j) * D_QK, (uint32_t)n_vis * krow_b);
+    const auto v_rs = dw_rsrc(p.vc + (row0 * n_kv + j) * D_V, (uint32_t)n_vis * vrow_b);
+    // V rows 32w .. 32w+31 -> LDS, three rows per instruction
+    {
+        const int v_lr = lane / DW_VCH, v_ch = lane % DW_VCH;
+        const bool v_on = v_lr < DW_VROWS_PER_COPY && v_ch < D_V / 8;
+        const uint32_t v_lane = v_lr * vrow_b + 16 * v_ch;
+#pragma unroll
+        for (int c = 0; c < DW_WAVE_COPIES; ++c) {
+            const int rw = 32 * uwave + DW_VROWS_PER_COPY * c;        // first row of this copy
+            if (v_on && DW_VROWS_PER_COPY * c + v_lr < 32)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(v_rs, (dw_lds_void_t *)(Vs + rw * DW_VROW), 16,
+                                                         v_lane + (uint32_t)rw * vrow_b, 0, 0, 0);
+        }
+    }
+    // K rows 32w + 16kb + r as A fragments: lane holds K[..][32kk + 8g .. +7]
+    bf16x8 ka[2][D_QK / 32];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int kk = 0; kk < D_QK / 32; ++kk)
+            ka[kb][kk] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                k_rs, (uint32_t)(32 * uwave + 16 * kb + r) * krow_b + 64 * kk + 16 * g, 0, 0));
+    // ---- scores: S^T = K Q^T, keys past the window masked by the initial value
+    f32x4 s[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s[kb][e] = 32 * uwave + 16 * kb + 4 * g + e < n_vis ? 0.f : -INFINITY;
+#pragma unroll
+        for (int kk = 0; kk < D_QK / 32; ++kk) s[kb] = mfma16(ka[kb][kk], qf[kk], s[kb]);
+    }
+    const float c_log2 = p.scale_log2;
+    {
+        const float mx = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                               fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+        const float wm = group4_max(mx);
+        if (g == 0) red_m[wave][r] = wm;
+    }
+    __syncthreads();
+    const float m = fmaxf(fmaxf(red_m[0][r], red_m[1][r]), fmaxf(red_m[2][r], red_m[3][r]));
+    const float m_ref = m == -INFINITY ? 0.f : m * c_log2;
+    uint32_t pw[4];
+    float l_part = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+        float pv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) pv[e] = fast_exp2(fmaf(s[kb][e], c_log2, -m_ref));
+        pw[2 * kb] = pack_bf16x2(pv[0], pv[1]);
+        pw[2 * kb + 1] = pack_bf16x2(pv[2], pv[3]);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) l_part = sum_bf16x2(pw[i], l_part);   // the bf16 weights P*V takes
+    const float wl = group4_sum(l_part);
+    if (g == 0) red_l[wave][r] = wl;
+    const bf16x8 pb = __builtin_bit_cast(bf16x8, u32x4{pw[0], pw[1], pw[2], pw[3]});
+
+    // ---- O^T += V^T P^T over this wave's 32 keys (V rows in LDS once this
+    // wave's copies have landed)
+    __builtin_amdgcn_s_waitcnt(0x0F70);            // vmcnt(0): this wave's copies are in LDS
+    const __bf16 *vrd = Vs + (32 * uwave + 4 * g + (r >> 2)) * DW_VROW + 8 * (r & 3);
+    f32x4 o[D_V / 16];
+#pragma unroll
+    for (int cb = 0; cb < D_V / 16; ++cb) {
+        const int cc = 32 * (cb >> 1) + 4 * (cb & 1);
+        const dw_s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((dw_lds_s16x4_t *)(vrd + cc));
+        const dw_s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((dw_lds_s16x4_t *)(vrd + 16 * DW_VROW + cc));
+        const dw_s16x4 v8[2] = {lo, hi};
+        o[cb] = mfma16(__builtin_bit_cast(bf16x8, v8), pb, f32x4{0.f, 0.f, 0.f, 0.f});
+    }
+    // this wave's partial sums over its own V rows (its reads are done: the
+    // products above consumed them): part[h][col], lane (r, g) holds columns
+    // 32c + 8g .. +7 of query r
+    float *part = reinterpret_cast<float *>(Vs + 32 * uwave * DW_VROW);
+    if (r < HEADS) {
+#pragma unroll
+        for (int c = 0; c < D_V / 32; ++c) {
+            *reinterpret_cast<f32x4 *>(part + r * D_V + 32 * c + 8 * g) = o[2 * c];
+            *reinterpret_cast<f32x4 *>(part + r * D_V + 32 * c + 8 * g + 4) = o[2 * c + 1];
+        }
+    }
+    __syncthreads();
+    if (tid >= 64) return;
+
+    // ---- combine and gate: signal head 4j + eh, columns ec .. ec+7
+    float ls = 0.f, ln = 0.f;
+#pragma unroll
+    for (int w = 0; w < DC_WAVES; ++w) {
+        ls += red_l[w][eh];
+        ln += red_l[w][GROUP];
+    }
+    float hs[8] = {0, 0, 0, 0, 0, 0, 0, 0}, hn[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+    for (int w = 0; w < DC_WAVES; ++w) {
+        const float *pw_ = reinterpret_cast<const float *>(Vs + 32 * w * DW_VROW);
+        const f32x4 s0 = *reinterpret_cast<const f32x4 *>(pw_ + eh * D_V + ec);
+        const f32x4 s1 = *reinterpret_cast<const f32x4 *>(pw_ + eh * D_V + ec + 4);
+        const f32x4 n0 = *reinterpret_cast<const f32x4 *>(pw_ + GROUP * D_V + ec);
+        const f32x4 n1 = *reinterpret_cast<const f32x4 *>(pw_ + GROUP * D_V + ec + 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            hs[e] += s0[e];
+            hs[4 + e] += s1[e];
+            hn[e] += n0[e];
+            hn[4 + e] += n1[e];
+        }
+    }
+    const float is = ls > 0.f ? 1.f / ls : 0.f, in = ln > 0.f ? 1.f / ln : 0.f;
+    const uint32_t lword = lw[eh >> 1];
+    const float lam = (eh & 1) ? bf16_hi(lword) : bf16_lo(lword);
+    float y[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const uint32_t gword = gw[e / 2];
+        const float gv = (e & 1) ? bf16_hi(gword) : bf16_lo(gword);
+        y[e] = gv * fmaf(-lam, hn[e] * in, hs[e] * is);
+    }
+    *reinterpret_cast<u32x4 *>(p.out + (orow0 + eh) * D_V + ec) =
+        u32x4{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]), pack_bf16x2(y[4], y[5]), pack_bf16x2(y[6], y[7])};
+}
+
 int decode_splits(int max_seqlen_k, int window) {
     const long vis = window > 0 ? (long)std::min(max_seqlen_k, window) : (long)max_seqlen_k;
     const long n = (vis + DC_CHUNK - 1) / DC_CHUNK;
@@ -294,6 +508,10 @@ hipError_t launch_decode(const void *qs, const void *qn, const void *kc, const v
     p.n_split = n_split;
     p.window = window;
     p.scale_log2 = scale * LOG2E;
+    if (window >= 1 && window <= DW_KEYS) {      // every query sees at most 128 keys: one workgroup each
+        hipLaunchKernelGGL(decode_window_kernel, dim3(n_kv, B), dim3(DC_THREADS), 0, stream, p);
+        return hipGetLastError();
+    }
     hipLaunchKernelGGL(decode_split_kernel, dim3(n_split, n_kv, B), dim3(DC_THREADS), 0, stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || n_split == 1) return e;

@@ -129,16 +129,22 @@ extern "C" size_t gdla_decode_workspace_size(int B, int n_kv, int max_seqlen_k, 
     return gdla::decode_workspace_bytes(B, n_kv, gdla::decode_splits(max_seqlen_k, window));
 }
 
-extern "C" int gdla_decode(const void *q_signal, const void *q_noise, const void *k_cache,
-                           const void *v_cache, const int32_t *cu_seqlens_k, int max_seqlen_k,
-                           const void *lambda_, const void *gate, void *out, void *workspace,
-                           size_t workspace_bytes, int B, int n_kv, int group, int d_qk, int d_v,
-                           int window, float softmax_scale, void *stream) {
-    g_last_error[0] = 0;
+namespace {
+
+// Checks of gdla_decode's arguments.  `workspace` is the area the split
+// partials go to; with `own_workspace` false its size and alignment are the
+// caller's to check.  Returns the status; on GDLA_OK, n_split and need are set.
+int check_decode(const void *q_signal, const void *q_noise, const void *k_cache, const void *v_cache,
+                 const int32_t *cu_seqlens_k, int max_seqlen_k, const void *lambda_, const void *gate,
+                 const void *out, const void *workspace, size_t workspace_bytes, bool own_workspace, int B,
+                 int n_kv, int group, int d_qk, int d_v, int window, float softmax_scale, int &n_split,
+                 size_t &need) {
     if (B < 0 || B > 65535) return fail(GDLA_ERR_INVALID_ARG, "B must be in [0, 65535] (got %d)", B);
     if (int rc = check_head_shape(n_kv, group, d_qk, d_v)) return rc;
     if (n_kv > 65535) return fail(GDLA_ERR_INVALID_ARG, "n_kv must be <= 65535 (got %d)", n_kv);
     if (int rc = check_scale_window(softmax_scale, window)) return rc;
+    n_split = 1;
+    need = 0;
     if (B == 0) return GDLA_OK;
     if (max_seqlen_k < 1) return fail(GDLA_ERR_INVALID_ARG, "max_seqlen_k must be >= 1 (got %d)", max_seqlen_k);
 
@@ -151,24 +157,49 @@ extern "C" int gdla_decode(const void *q_signal, const void *q_noise, const void
     if (!cu_seqlens_k) return fail(GDLA_ERR_INVALID_ARG, "cu_seqlens_k is NULL");
     if (!aligned(cu_seqlens_k, 4)) return fail(GDLA_ERR_MISALIGNED, "cu_seqlens_k is not 4-byte aligned");
 
-    const int n_split = gdla::decode_splits(max_seqlen_k, window);
-    const size_t need = gdla::decode_workspace_bytes(B, n_kv, n_split);
-    if (need > 0) {
+    n_split = gdla::decode_splits(max_seqlen_k, window);
+    need = gdla::decode_workspace_bytes(B, n_kv, n_split);
+    if (need > 0 && own_workspace) {
         if (!workspace) return fail(GDLA_ERR_WORKSPACE, "workspace is NULL, %zu bytes needed", need);
         if (workspace_bytes < need)
             return fail(GDLA_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
         if (!aligned(workspace, 16)) return fail(GDLA_ERR_MISALIGNED, "workspace is not 16-byte aligned");
     }
+    // the inputs whose extent the call knows (the caches' row count is not an
+    // argument), the output and the workspace the split kernel writes
     const uintptr_t ns = (uintptr_t)n_kv * group;
     const Range o = {"out", (uintptr_t)out, (uintptr_t)out + (uintptr_t)B * ns * d_v * 2};
-    const Range in[4] = {
+    const Range w = {"workspace", (uintptr_t)workspace, (uintptr_t)workspace + need};
+    const Range in[5] = {
         {"q_signal", (uintptr_t)q_signal, (uintptr_t)q_signal + (uintptr_t)B * ns * d_qk * 2},
         {"q_noise", (uintptr_t)q_noise, (uintptr_t)q_noise + (uintptr_t)B * n_kv * d_qk * 2},
         {"lambda", (uintptr_t)lambda_, (uintptr_t)lambda_ + (uintptr_t)B * ns * 2},
-        {"gate", (uintptr_t)gate, (uintptr_t)gate + (uintptr_t)B * ns * d_v * 2}};
-    for (const Range &x : in)
+        {"gate", (uintptr_t)gate, (uintptr_t)gate + (uintptr_t)B * ns * d_v * 2},
+        {"cu_seqlens_k", (uintptr_t)cu_seqlens_k, (uintptr_t)cu_seqlens_k + ((uintptr_t)B + 1) * 4}};
+    for (const Range &x : in) {
         if (overlaps(o, x)) return fail(GDLA_ERR_INVALID_ARG, "out overlaps %s", x.name);
+        if (own_workspace && need > 0 && overlaps(w, x))
+            return fail(GDLA_ERR_INVALID_ARG, "workspace overlaps %s", x.name);
+    }
+    if (own_workspace && need > 0 && overlaps(o, w)) return fail(GDLA_ERR_INVALID_ARG, "out overlaps workspace");
+    return GDLA_OK;
+}
 
+}  // namespace
+
+extern "C" int gdla_decode(const void *q_signal, const void *q_noise, const void *k_cache,
+                           const void *v_cache, const int32_t *cu_seqlens_k, int max_seqlen_k,
+                           const void *lambda_, const void *gate, void *out, void *workspace,
+                           size_t workspace_bytes, int B, int n_kv, int group, int d_qk, int d_v,
+                           int window, float softmax_scale, void *stream) {
+    g_last_error[0] = 0;
+    int n_split = 1;
+    size_t need = 0;
+    if (int rc = check_decode(q_signal, q_noise, k_cache, v_cache, cu_seqlens_k, max_seqlen_k, lambda_, gate, out,
+                              workspace, workspace_bytes, true, B, n_kv, group, d_qk, d_v, window, softmax_scale,
+                              n_split, need))
+        return rc;
+    if (B == 0) return GDLA_OK;
     hipError_t e = gdla::launch_decode(q_signal, q_noise, k_cache, v_cache, cu_seqlens_k, lambda_,
                                        gate, out, workspace, B, n_kv, n_split, window, softmax_scale,
                                        static_cast<hipStream_t>(stream));
@@ -222,13 +253,14 @@ extern "C" int gdla_decode_latent(const void *q_signal, const void *q_noise, con
     const Range o = {"out", (uintptr_t)out, (uintptr_t)out + (uintptr_t)B * ns * d_v * 2};
     const Range w = {"workspace", (uintptr_t)workspace, (uintptr_t)workspace + need};
     const int d_qk = d_v + d_r;                  // the content part of a query is d_v = 128 values
-    const Range in[6] = {
+    const Range in[7] = {
         {"q_signal", (uintptr_t)q_signal, (uintptr_t)q_signal + (uintptr_t)B * ns * d_qk * 2},
         {"q_noise", (uintptr_t)q_noise, (uintptr_t)q_noise + (uintptr_t)B * n_kv * d_qk * 2},
         {"w_uk", (uintptr_t)w_uk, (uintptr_t)w_uk + (uintptr_t)n_kv * 128 * d_c * 2},
         {"w_uv", (uintptr_t)w_uv, (uintptr_t)w_uv + (uintptr_t)n_kv * d_v * d_c * 2},
         {"lambda", (uintptr_t)lambda_, (uintptr_t)lambda_ + (uintptr_t)B * ns * 2},
-        {"gate", (uintptr_t)gate, (uintptr_t)gate + (uintptr_t)B * ns * d_v * 2}};
+        {"gate", (uintptr_t)gate, (uintptr_t)gate + (uintptr_t)B * ns * d_v * 2},
+        {"cu_seqlens_k", (uintptr_t)cu_seqlens_k, (uintptr_t)cu_seqlens_k + ((uintptr_t)B + 1) * 4}};
     for (const Range &x : in) {
         if (overlaps(o, x)) return fail(GDLA_ERR_INVALID_ARG, "out overlaps %s", x.name);
         if (overlaps(w, x)) return fail(GDLA_ERR_INVALID_ARG, "workspace overlaps %s", x.name);

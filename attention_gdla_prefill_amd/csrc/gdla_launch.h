@@ -29,7 +29,7 @@ hipError_t launch_decode(const void *qs, const void *qn, const void *kc, const v
                          void *workspace, int B, int n_kv, int n_split, int window, float scale,
                          hipStream_t stream);
 
-// Latent-cache decode: splits per sequence, workspace bytes, launch (3 kernels).
+// Backward: workspace bytes, launch (the saving forward and the gradient kernels).
 size_t backward_workspace_bytes(int B, int T, int n_kv);
 hipError_t launch_backward(const void *qs, const void *qn, const void *k, const void *v, const void *lam,
                            const void *gate, const void *dout, void *dqs, void *dqn, void *dk, void *dv,
@@ -41,6 +41,7 @@ hipError_t launch_prep(void *q_signal, void *q_noise, const void *k_rope, void *
                        const void *w_lambda, void *lambda_out, const void *gate_pre, void *gate_out,
                        int B, int T, int n_kv, int d_model, int pos0, float rope_theta, hipStream_t stream);
 
+// Latent-cache decode: splits per sequence, workspace bytes, launch.
 int latent_splits(int max_seqlen_k, int window);
 size_t latent_workspace_bytes(int B, int n_kv, int n_split);
 hipError_t launch_decode_latent(const void *qs, const void *qn, const void *lat, const int32_t *cu,

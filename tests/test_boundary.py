@@ -130,6 +130,31 @@ def test_decode_rejections(lib):
     assert decode(lib, max_len=65536, ws=A + 0x800000008, ws_bytes=need) == MISALIGNED
 
 
+def test_decode_rejects_overlapping_workspace(lib):
+    """The split kernel writes partials into the workspace: it may not overlap
+    the output or any input whose extent the call knows."""
+    need = lib.gdla_decode_workspace_size(2, 16, 65536, 0)
+    ws = A + 0x800000000
+    ptrs = [A + k * (1 << 32) for k in range(7)]
+    for i, name in ((0, b"q_signal"), (1, b"q_noise"), (4, b"lambda"), (5, b"gate")):
+        bad = list(ptrs)
+        bad[i] = ws + 4096                     # input inside the workspace
+        assert decode(lib, bad, max_len=65536, ws=ws, ws_bytes=need) == INVALID
+        assert b"workspace overlaps" in lib.gdla_last_error() and name in lib.gdla_last_error()
+    bad = list(ptrs)
+    bad[6] = ws + need - 16                    # output runs into the workspace's end
+    assert decode(lib, bad, max_len=65536, ws=ws, ws_bytes=need) == INVALID
+    assert b"out overlaps workspace" in lib.gdla_last_error()
+    assert decode(lib, max_len=65536, cu=ws + 64, ws=ws, ws_bytes=need) == INVALID
+    assert b"cu_seqlens_k" in lib.gdla_last_error()
+    bad = list(ptrs)
+    bad[6] = A + 0x700000000                   # output over the sequence offsets
+    assert decode(lib, bad, window=128) == INVALID
+    assert b"out overlaps cu_seqlens_k" in lib.gdla_last_error()
+    # a window that needs no workspace ignores the pointer
+    assert lib.gdla_decode_workspace_size(2, 16, 65536, 128) == 0
+
+
 def test_decode_empty_is_noop(lib):
     assert decode(lib, [None] * 7, cu=None, B=0) == OK
 
