@@ -11,6 +11,30 @@ import oracle
 # Parity bar after the gate (relative L2 over the compared elements, and max abs).
 REL_L2 = 1e-2
 MAX_ABS = 3e-2
+# Sharper bars on top of those two, so that a defect confined to a few rows or
+# elements cannot hide in the global figures:
+#  * max abs error <= 3e-2 of the largest |expected| value (the absolute 3e-2
+#    is vacuous when outputs are ~3e-4);
+#  * every output row (the 128 values of one (token, head)) within 5e-2
+#    relative L2.  A row's denominator is at least a quarter of the RMS row
+#    norm over the heads of its own token: where lambda is near 1 and the two
+#    softmax outputs nearly agree (the configured, almost uniform logits),
+#    D = H_S - lambda*H_N cancels to a small row that still carries the
+#    absolute rounding error of the bf16 weights of both paths (about 2^-9 of
+#    |H|), which is small only against the token's other heads.
+# On the configured distribution (logit spread ~0.005) H_S and H_N differ by
+# less than the bf16 rounding of their weights, so rows that cancel keep a
+# larger relative error even against the floor: their row bar is 1e-1 (the
+# global rel-L2 and max-abs bars are the same for every distribution).
+MAX_ABS_REL = 3e-2
+ROW_REL = 5e-2
+ROW_REL_CFG = 1e-1
+ROW_FLOOR = 0.25
+
+
+def row_bound(dist):
+    """Worst-row bar for a named input distribution."""
+    return ROW_REL_CFG if dist == "cfg" else ROW_REL
 
 
 def log(msg):
@@ -25,24 +49,34 @@ def f32(t):
     return t.detach().float().cpu().numpy()
 
 
-def compare(got, want, what=""):
+def compare(got, want, what="", row_rel=ROW_REL):
     """got: bf16/float tensor or array, want: float64 array of the same shape."""
     g = got.detach().double().cpu().numpy() if isinstance(got, torch.Tensor) else np.asarray(got, np.float64)
-    w = np.asarray(want, np.float64)
+    w = want.detach().double().cpu().numpy() if isinstance(want, torch.Tensor) else np.asarray(want, np.float64)
     assert g.shape == w.shape, (g.shape, w.shape)
     assert np.isfinite(g).all(), "%s: non-finite values in the GPU output" % what
+    assert np.isfinite(w).all(), "%s: non-finite values in the expected output" % what
     diff = g - w
     nw = np.linalg.norm(w)
     rel = np.linalg.norm(diff) / nw if nw > 0 else np.linalg.norm(diff)
     mabs = float(np.max(np.abs(diff))) if diff.size else 0.0
-    # worst row: last dim is d_v
-    rows_d = diff.reshape(-1, diff.shape[-1])
-    rows_w = w.reshape(-1, w.shape[-1])
-    rn = np.linalg.norm(rows_w, axis=1)
-    worst = float(np.max(np.linalg.norm(rows_d, axis=1) / np.maximum(rn, 1e-30))) if rn.size else 0.0
-    log("%s: rel_l2=%.3e max_abs=%.3e worst_row_rel=%.3e" % (what, rel, mabs, worst))
+    wmax = float(np.max(np.abs(w))) if w.size else 0.0
+    # worst row: last dim is d_v, the one before it the heads of a token
+    n_h = w.shape[-2] if w.ndim >= 2 else 1
+    rows_d = diff.reshape(-1, n_h, diff.shape[-1])
+    rows_w = w.reshape(-1, n_h, w.shape[-1])
+    rn = np.linalg.norm(rows_w, axis=2)                                   # [tokens, heads]
+    floor = ROW_FLOOR * np.sqrt(np.mean(rn ** 2, axis=1, keepdims=True)) if rn.size else rn
+    den = np.maximum(np.maximum(rn, floor), 1e-30)
+    row_err = (np.linalg.norm(rows_d, axis=2) / den).reshape(-1) if rn.size else np.zeros(0)
+    rn = rn.reshape(-1)
+    worst = float(np.max(row_err)) if rn.size else 0.0
+    log("%s: rel_l2=%.3e max_abs=%.3e (%.3e of max|want|) worst_row_rel=%.3e (row %d)"
+        % (what, rel, mabs, mabs / max(wmax, 1e-30), worst, int(np.argmax(row_err)) if rn.size else -1))
     assert rel <= REL_L2, "%s: rel_l2 %.3e > %.0e" % (what, rel, REL_L2)
     assert mabs <= MAX_ABS, "%s: max_abs %.3e > %.0e" % (what, mabs, MAX_ABS)
+    assert mabs <= MAX_ABS_REL * wmax, "%s: max_abs %.3e > %.0e * max|want| %.3e" % (what, mabs, MAX_ABS_REL, wmax)
+    assert worst <= row_rel, "%s: worst row rel %.3e > %.0e" % (what, worst, row_rel)
     return rel, mabs, worst
 
 
@@ -71,15 +105,30 @@ def oracle_prefill_rows(x, window, rb, rt, scale=None):
 
 
 def stratified_rows(B, T, n_first, n_last, n_mid, seed):
+    """Per sequence: the first n_first and last n_last positions, and n_mid
+    distinct random positions between them."""
     r = np.random.default_rng(seed)
     rows = []
     for b in range(B):
         ts = set(range(min(n_first, T))) | set(range(max(0, T - n_last), T))
         if T > n_first + n_last:
-            ts |= set(r.integers(n_first, T - n_last, size=n_mid).tolist())
+            mid = np.arange(n_first, T - n_last)
+            ts |= set(r.choice(mid, size=min(n_mid, mid.size), replace=False).tolist())
         rows += [(b, t) for t in sorted(ts)]
     rows = np.array(rows, dtype=np.int32)
     return rows[:, 0].copy(), rows[:, 1].copy()
+
+
+def oracle_prefill_rows_long(x, window, rb, rt, scale=None):
+    """The float64 torch row oracle (for sequences too long for the C oracle
+    to check 2,048 rows in seconds); x's tensors may live on the GPU."""
+    from oracle import rows as orows
+    dev = x["q_signal"].device
+    rb_t = torch.as_tensor(rb, dtype=torch.long, device=dev)
+    rt_t = torch.as_tensor(rt, dtype=torch.long, device=dev)
+    pick = lambda t: t[rb_t, rt_t].cpu()
+    return orows.prefill_rows(x["k"], x["v"], pick(x["q_signal"]), pick(x["q_noise"]), pick(x["lam"]),
+                              pick(x["gate"]), rb, rt, window=window, scale=scale)
 
 
 def gpu_decode(d, max_len, window, scale=None):

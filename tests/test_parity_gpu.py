@@ -16,9 +16,9 @@ import pytest
 import torch
 
 import workload as W
-from gdla_testutil import (compare, default_scale, gpu_decode, gpu_prefill, gpu_prefill_prefix, log,
-                           oracle_decode, oracle_prefill, oracle_prefill_rows, query_tail,
-                           stratified_rows, to_dev)
+from gdla_testutil import (ROW_REL_CFG, compare, default_scale, row_bound, gpu_decode, gpu_prefill, gpu_prefill_prefix, log,
+                           oracle_decode, oracle_prefill, oracle_prefill_rows, oracle_prefill_rows_long,
+                           query_tail, stratified_rows, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -48,7 +48,7 @@ def test_tiny_config():
     w = W.WORKLOADS["tiny"]
     log("tiny T=256 n_kv=1 full")
     x = to_dev(W.prefill_inputs(w, seed=0))
-    compare(gpu_prefill(x, 0), oracle_prefill(x, 0), "tiny")
+    compare(gpu_prefill(x, 0), oracle_prefill(x, 0), "tiny", row_rel=ROW_REL_CFG)
 
 
 CASES = [
@@ -70,7 +70,8 @@ def test_prefill_parity_small(B, T, n_kv, window, dist):
     kw = {"cfg": {}, "sharp": SHARP, "sharper": SHARPER}[dist]
     log("prefill B=%d T=%d n_kv=%d window=%d dist=%s" % (B, T, n_kv, window, dist))
     x = to_dev(W.prefill_inputs(small(B, T, n_kv), seed=T + window, **kw))
-    compare(gpu_prefill(x, window), oracle_prefill(x, window), "B%d T%d W%d %s" % (B, T, window, dist))
+    compare(gpu_prefill(x, window), oracle_prefill(x, window), "B%d T%d W%d %s" % (B, T, window, dist),
+            row_rel=row_bound(dist))
 
 
 @pytest.mark.parametrize("direction", ["growing", "shrinking"])
@@ -110,6 +111,15 @@ def test_prefill_deterministic():
     a = gpu_prefill(x, 0)
     b = gpu_prefill(x, 0)
     assert torch.equal(a, b)
+
+
+def test_sync_check_mode(monkeypatch):
+    """GDLA_SYNC_CHECK=1: every call waits for its kernels; results unchanged."""
+    monkeypatch.setenv("GDLA_SYNC_CHECK", "1")
+    x = to_dev(W.prefill_inputs(small(1, 130, 2), seed=13, **SHARP))
+    compare(gpu_prefill(x, 0), oracle_prefill(x, 0), "sync-check prefill")
+    d = decode_case([5, 3000, 64], 2, seed=14, **SHARP)
+    compare(gpu_decode(d, 3000, 0), oracle_decode(d, 0), "sync-check decode")
 
 
 def test_prefill_window_ge_T_equals_full():
@@ -173,7 +183,7 @@ def test_pf_full_4k_sampled():
     out = gpu_prefill(x, 0)
     rb, rt = stratified_rows(w.B, w.T, 64, 64, 128, seed=1)
     compare(out[torch.as_tensor(rb).long(), torch.as_tensor(rt).long()],
-            oracle_prefill_rows(x, 0, rb, rt), "pf_full_4k rows=%d" % len(rb))
+            oracle_prefill_rows(x, 0, rb, rt), "pf_full_4k rows=%d" % len(rb), row_rel=ROW_REL_CFG)
 
 
 def test_pf_full_4k_sharp_sampled():
@@ -193,7 +203,71 @@ def test_pf_swa_32k_sampled():
     out = gpu_prefill(x, w.window)
     rb, rt = stratified_rows(w.B, w.T, 200, 64, 512, seed=3)
     compare(out[torch.as_tensor(rb).long(), torch.as_tensor(rt).long()],
-            oracle_prefill_rows(x, w.window, rb, rt), "pf_swa_32k rows=%d" % len(rb))
+            oracle_prefill_rows(x, w.window, rb, rt), "pf_swa_32k rows=%d" % len(rb), row_rel=ROW_REL_CFG)
+
+
+def test_pf_swa_32k_sharp_sampled():
+    """The 32K window layer (B=2) with logit spread ~1."""
+    w = W.WORKLOADS["pf_swa_32k"]
+    log("pf_swa_32k sharp sampled")
+    x = W.prefill_inputs(w, seed=4, device="cuda", **SHARP)
+    out = gpu_prefill(x, w.window)
+    rb, rt = stratified_rows(w.B, w.T, 200, 64, 512, seed=5)
+    compare(out[torch.as_tensor(rb).long(), torch.as_tensor(rt).long()],
+            oracle_prefill_rows(x, w.window, rb, rt), "pf_swa_32k sharp rows=%d" % len(rb))
+    del x, out
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("dist", ["cfg", "sharp"])
+def test_pf_full_128k_sampled(dist):
+    """The 128K full-causal layer (B=1, 16 KV heads), launched as the benchmark
+    launches it: 2,048 rows, all 80 heads -- the first and last 128 positions
+    and 1,792 distinct random positions between -- against the float64 row
+    oracle."""
+    kw = {"cfg": {}, "sharp": SHARP}[dist]
+    w = W.WORKLOADS["pf_full_128k"]
+    log("pf_full_128k sampled %s" % dist)
+    x = W.prefill_inputs(w, seed=0 if dist == "cfg" else 6, device="cuda", **kw)
+    out = gpu_prefill(x, 0)
+    rb, rt = stratified_rows(w.B, w.T, 128, 128, 1792, seed=7)
+    assert len(rt) == 2048
+    got = out[torch.as_tensor(rb, device="cuda").long(), torch.as_tensor(rt, device="cuda").long()].cpu()
+    del out
+    torch.cuda.empty_cache()
+    want = oracle_prefill_rows_long(x, 0, rb, rt)
+    compare(got, want, "pf_full_128k %s rows=%d" % (dist, len(rt)), row_rel=row_bound(dist))
+    del x
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("direction", ["growing", "shrinking"])
+def test_prefill_steep_logits_window_runs(direction):
+    """The exact-maxima redo inside runs of query tiles: B=1, T=16384, 16 KV
+    heads, a 128-key window (a workgroup walks 8 consecutive query tiles whose
+    next copies are in flight).  Keys carry a sawtooth of period 512 in one
+    dimension, rising or falling by 2 natural units per key against a query
+    value of 16 (scale 1): falling teeth peak at the oldest key of every
+    window, rising ones wherever a window straddles a tooth's end, so most
+    query tiles are redone against their exact maxima.  Whole runs (their
+    boundaries included) and random rows are compared."""
+    w = W.Workload("steep", "prefill", B=1, T=16384, n_kv=16, window=128)
+    log("prefill steep logits window runs %s" % direction)
+    x = W.prefill_inputs(w, seed=9, device="cuda", **SHARP)
+    pos = torch.arange(w.T, device="cuda") % 512
+    tooth = (pos if direction == "growing" else 512 - pos).float() / 8
+    x["q_signal"][..., 0] = 16.0
+    x["q_noise"][..., 0] = 16.0
+    x["k"][0, :, :, 0] = tooth.to(torch.bfloat16)[:, None]
+    out = gpu_prefill(x, w.window, scale=1.0)
+    rt = np.concatenate([np.arange(0, 24 * 64), np.arange(120 * 64, 136 * 64), np.arange(w.T - 200, w.T),
+                         np.random.default_rng(10).integers(0, w.T, 256)]).astype(np.int32)
+    rt = np.unique(rt)
+    rb = np.zeros_like(rt)
+    compare(out[torch.as_tensor(rb).long(), torch.as_tensor(rt).long()],
+            oracle_prefill_rows(x, w.window, rb, rt, scale=1.0), "steep window runs %s rows=%d" % (direction, len(rt)))
+    del x, out
+    torch.cuda.empty_cache()
 
 
 @pytest.mark.parametrize("window,dist", [(128, "cfg"), (128, "sharp"), (1, "sharp"), (64, "sharp"),
@@ -212,7 +286,8 @@ def test_prefill_window_runs_sampled(window, dist):
     rt = np.unique(rt)
     rb = np.zeros_like(rt)
     compare(out[torch.as_tensor(rb).long(), torch.as_tensor(rt).long()],
-            oracle_prefill_rows(x, window, rb, rt), "runs W%d %s rows=%d" % (window, dist, len(rt)))
+            oracle_prefill_rows(x, window, rb, rt), "runs W%d %s rows=%d" % (window, dist, len(rt)),
+            row_rel=row_bound(dist))
 
 
 # ---------------------------------------------------------------------------
@@ -232,7 +307,7 @@ def test_decode_parity_small(window, dist):
     log("decode small window=%d dist=%s" % (window, dist))
     d = decode_case(lengths, 2, seed=window + 1, **kw)
     compare(gpu_decode(d, max(lengths), window), oracle_decode(d, window),
-            "decode W%d %s" % (window, dist))
+            "decode W%d %s" % (window, dist), row_rel=row_bound(dist))
 
 
 @pytest.mark.parametrize("window", [0, 128])
@@ -278,7 +353,46 @@ def test_decode_configs_sampled(name):
                "k_cache": d["k_cache"][lo:hi], "v_cache": d["v_cache"][lo:hi],
                "cu_seqlens": torch.tensor([0, hi - lo], dtype=torch.int32),
                "lam": d["lam"][b:b + 1], "gate": d["gate"][b:b + 1]}
-        compare(out[b:b + 1], oracle_decode(one, w.window), "%s seq %d L=%d" % (name, b, hi - lo))
+        compare(out[b:b + 1], oracle_decode(one, w.window), "%s seq %d L=%d" % (name, b, hi - lo),
+                row_rel=ROW_REL_CFG)
+
+
+def one_sequence(d, b, cu, window):
+    """Decode inputs of sequence b alone, with only the cache rows its query
+    sees (the last `window` rows with a window; positions do not enter the
+    scores, so a shorter cache of the same rows is the same problem)."""
+    lo, hi = int(cu[b]), int(cu[b + 1])
+    if window > 0:
+        lo = max(lo, hi - window)
+    return {"q_signal": d["q_signal"][b:b + 1], "q_noise": d["q_noise"][b:b + 1],
+            "k_cache": d["k_cache"][lo:hi], "v_cache": d["v_cache"][lo:hi],
+            "cu_seqlens": torch.tensor([0, hi - lo], dtype=torch.int32),
+            "lam": d["lam"][b:b + 1], "gate": d["gate"][b:b + 1]}
+
+
+@pytest.mark.parametrize("name", ["dec_full", "dec_swa"])
+def test_decode_configs_sharp(name):
+    """The 64-sequence decodes with Q, K ~ N(0,1) (logit spread ~1, so that
+    QK^T and the merge of the splits decide the result).  Window: every
+    sequence is checked.  Full causal: the three longest (near 65,536 keys:
+    32 splits merged), the two shortest, and the first, middle and last."""
+    w = W.WORKLOADS[name]
+    log("%s sharp" % name)
+    d = W.decode_inputs(w, seed=4, device="cuda", **SHARP)
+    lengths = d["lengths"]
+    max_len = int(lengths.max())
+    out = gpu_decode(d, max_len, w.window)
+    cu = d["cu_seqlens"].cpu().long()
+    if w.window > 0:
+        pick = list(range(w.B))
+    else:
+        order = torch.argsort(lengths).tolist()
+        pick = sorted(set(order[-3:] + order[:2] + [0, w.B // 2, w.B - 1]))
+    for b in pick:
+        one = one_sequence(d, b, cu, w.window)
+        compare(out[b:b + 1], oracle_decode(one, 0), "%s sharp seq %d L=%d" % (name, b, int(lengths[b])))
+    del d, out
+    torch.cuda.empty_cache()
 
 
 # ---------------------------------------------------------------------------
@@ -305,7 +419,7 @@ def test_prefill_prefix_matches_oracle_and_full_rows(case):
     rb = np.repeat(np.arange(B, dtype=np.int32), Tq)
     rt = np.tile(np.arange(P, P + Tq, dtype=np.int32), B)
     want = oracle_prefill_rows(x, window, rb, rt).reshape(B, Tq, 4 * n_kv, 128)
-    compare(got, want, "prefix P=%d Tq=%d W=%d" % (P, Tq, window))
+    compare(got, want, "prefix P=%d Tq=%d W=%d" % (P, Tq, window), row_rel=row_bound(dist))
     # the same query tiles and key tiles as the whole-sequence call: the same rows, bit for bit
     assert torch.equal(got, gpu_prefill(x, window)[:, P:])
 
