@@ -1,20 +1,25 @@
 """Benchmark of the GDLA attention core on one MI355X.
 
-One step = one pass of the fused prefill kernel over the full-causal workload
-(batch 1, T = 4096, 16 KV heads / 64 signal / 16 noise heads, qk 192 / v 128,
-bf16, synthetic seeded inputs already resident in HBM).  The kernel does the
-whole hot path: band limits, K/V tiles, QK^T, mask, softmax, PV, the
-differential combine and the gate.
+One step = one pass of the fused prefill kernel over the long-context
+full-causal workload (batch 1, T = 131072, 16 KV heads / 64 signal / 16 noise
+heads, qk 192 / v 128, bf16, synthetic seeded inputs already resident in HBM).
+The kernel does the whole hot path: band limits, K/V tiles, QK^T, mask,
+softmax, PV, the differential combine and the gate.
+
+Before the timed steps the kernel runs untimed until at least --warmup
+launches and --settle-s seconds of steady work have passed (the GPU clock
+needs about a tenth of a second of load to settle); the JSON reports both.
 
 Printed: ONE JSON line with the throughput (unmasked FLOPs / time), the
 roofline of the prefill kernel (timed with HIP events on the stream it runs
-on), the CPU oracle timed on a bounded sample of the same workload, and the
-other workloads (sliding-window prefill, 128K prefill, prefill after a
-prefix, decode over the expanded and the latent cache, the pre-attention step)
+on), the roofline of the full-causal decode (cold cache, HBM-bound), the fp32
+CPU oracle timed on a bounded sample of the same workload (extrapolated by
+unmasked pairs) and in full on the small configs, and the other workloads
 under "extra".
 
-    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--no-extra]
-                    [--extras pf_swa_32k,dec_full,...]
+    python bench.py [--steps K] [--warmup W] [--settle-s S] [--workload NAME]
+                    [--no-cpu-baseline] [--cpu-full] [--no-decode] [--no-extra]
+                    [--extras a,b,...]
 """
 import argparse
 import glob
@@ -65,14 +70,30 @@ def decode_latent_bytes(lengths, window, n_kv=16, n_sig=64):
     return sum(vis) * 576 * 2 + len(lengths) * per_seq + weights + 4 * (len(lengths) + 1)
 
 
-PREFILL_SOURCES = ("prefill_gfx950.hip", "gdla_device.h")
+# kernels and sources behind each workload's traffic figures: the figures
+# hold while these sources are unchanged
+TRAFFIC_SOURCES = {
+    "prefill": ("prefill_gfx950.hip", "gdla_device.h"),
+    "decode": ("decode_gfx950.hip", "gdla_device.h"),
+}
 
 
-def source_hash():
-    """Hash of the files the prefill kernel is built from (its traffic figures
-    hold while these are unchanged)."""
+def traffic_kind(workload):
+    return "decode" if workload.startswith("dec_") else "prefill"
+
+
+def traffic_kernels(workload):
+    if workload == "dec_swa":
+        return ("decode_window_kernel",)
+    if workload.startswith("dec_"):
+        return ("decode_split_kernel", "decode_combine_kernel")
+    return ("prefill_kernel",)
+
+
+def source_hash(kind="prefill"):
+    """Hash of the files a workload's kernels are built from."""
     h = hashlib.sha256()
-    for name in PREFILL_SOURCES:
+    for name in TRAFFIC_SOURCES[kind]:
         h.update(open(os.path.join(ROOT, "attention_gdla_prefill_amd", "csrc", name), "rb").read())
     return h.hexdigest()[:16]
 
@@ -93,23 +114,31 @@ def _counter_rows(run_dir, counter):
 
 def record_traffic(workload, fetch_dir, write_dir):
     """Writes profiles/traffic_<workload>.json from two counter runs of
-    `bench.py --workload <workload> --steps 5 --warmup 2 --no-cpu-baseline
-    --no-extra --copy-probe` (FETCH_SIZE, then WRITE_SIZE): the prefill
-    kernel's median per dispatch, each counter scaled by what it reads for the
-    1 GiB device copy that ends the run."""
+    `bench.py --workload <workload> --steps 3 --warmup 1 --settle-s 0
+    --no-cpu-baseline --no-decode --no-extra --copy-probe` (FETCH_SIZE, then
+    WRITE_SIZE): per kernel of the workload the median per dispatch, summed
+    over its kernels, each counter scaled by what it reads for the 1 GiB
+    device copy that ends the run."""
     import statistics
-    out = {"kernel": "prefill_kernel", "workload": workload, "source_hash": source_hash()}
+    kind = traffic_kind(workload)
+    kernels = traffic_kernels(workload)
+    out = {"kernels": list(kernels), "workload": workload, "source_hash": source_hash(kind)}
     scaled = {}
     for key, run_dir, counter in (("fetch", fetch_dir, "FETCH_SIZE"), ("write", write_dir, "WRITE_SIZE")):
         rows = _counter_rows(run_dir, counter)
-        kern = [v for n, v in rows if "prefill_kernel" in n]
         copy = [v for n, v in rows if "copy" in n.lower()]
-        if not kern or not copy:
-            raise SystemExit("%s: prefill or copy dispatches missing" % run_dir)
-        per = statistics.median(kern)
+        if not copy:
+            raise SystemExit("%s: copy dispatch missing" % run_dir)
+        per = 0.0
+        for kname in kernels:
+            vals = [v for n, v in rows if kname in n]
+            if not vals:
+                raise SystemExit("%s: no %s dispatches" % (run_dir, kname))
+            out["%s_kib_per_dispatch_%s" % (key, kname)] = statistics.median(vals)
+            per += statistics.median(vals)
         probe = copy[-1]
         scale = (1 << 30) / 1024.0 / probe
-        out["%s_kib_per_dispatch" % key] = per
+        out["%s_kib_per_launch" % key] = per
         out["%s_scale" % key] = scale
         out["copy_probe_%s_kib" % key] = probe
         scaled[key] = per * 1024.0 * scale
@@ -122,12 +151,32 @@ def record_traffic(workload, fetch_dir, write_dir):
     print(json.dumps(out))
 
 
-def time_kernel(fn, steps, warmup, stream):
-    """Run fn warmup+steps times; return (wall ms/step, per-launch HIP-event ms list)."""
+def load_traffic(name):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they
+    were taken on the current kernel sources (else None)."""
+    p = os.path.join(ROOT, "profiles", "traffic_%s.json" % name)
+    if not os.path.exists(p):
+        return None
+    t = json.load(open(p))
+    if t.get("source_hash") != source_hash(traffic_kind(name)):
+        return None
+    return t.get("bytes_per_launch")
+
+
+def time_kernel(fn, steps, warmup, stream, settle_s=0.0):
+    """Run fn untimed until at least `warmup` launches and `settle_s` seconds
+    of steady work have passed, then `steps` timed launches.  Returns (wall
+    ms/step, per-launch HIP-event ms list, settle record)."""
     import torch
-    for _ in range(warmup):
+    t0 = time.perf_counter()
+    n = 0
+    while n < warmup or time.perf_counter() - t0 < settle_s:
         fn()
+        n += 1
+        if n % 4 == 0 or n >= warmup:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
+    settle = {"launches": n, "seconds": round(time.perf_counter() - t0, 3)}
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(steps)]
     t0 = time.perf_counter()
@@ -137,49 +186,164 @@ def time_kernel(fn, steps, warmup, stream):
         b.record(stream)
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) * 1e3 / steps
-    return wall, [a.elapsed_time(b) for a, b in ev]
+    return wall, [a.elapsed_time(b) for a, b in ev], settle
 
 
-def cpu_baseline(budget_s=15.0):
-    """The oracle, untuned, on a random sample of query rows of the 4K workload."""
+COLD = ("cold: a 512 MB buffer (twice the 256 MB Infinity Cache) is read before each launch, so the "
+        "launch's inputs are in no cache and no dirty line is left for it to write back")
+
+
+def cold_times(call, steps, warmup):
+    """Median and per-launch HIP-event times (ms) of `call` with cold caches:
+    before each launch a 512 MB buffer is read (a sum over it), which evicts
+    the L2s and the Infinity Cache without leaving dirty lines.  Also the
+    median with the older protocol, a 512 MB buffer *written* before each
+    launch: that leaves up to the Infinity Cache's size of dirty lines, which
+    the timed launch then writes back (reported for comparison only)."""
+    import torch
+    stream = torch.cuda.current_stream()
+    sweep = torch.ones(128 << 20, dtype=torch.float32, device="cuda")
+    dirty = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    res = {}
+    for mode in ("clean", "dirty"):
+        times = []
+        for _ in range(steps):
+            if mode == "clean":
+                sweep.sum()
+            else:
+                dirty.fill_(1)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            call()
+            b.record(stream)
+            torch.cuda.synchronize()
+            times.append(a.elapsed_time(b))
+        res[mode] = sorted(times)[len(times) // 2]
+    del sweep, dirty
+    torch.cuda.empty_cache()
+    return res["clean"], res["dirty"]
+
+
+def cpu_info():
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return model, os.cpu_count()
+
+
+def cpu_baseline_headline(x, w, budget_s=15.0):
+    """The fp32 oracle, untuned, on random query rows (all 80 heads) of the
+    headline workload's own inputs (copied from the GPU), extrapolated to the
+    whole launch by unmasked (query, key) pairs."""
+    import numpy as np
+    import torch
+    import oracle
+    lib = oracle.library_fp32()
+    k = x["k"].float().cpu().numpy()
+    v = x["v"].float().cpu().numpy()
+    rng = np.random.default_rng(0)
+    n, rows, pairs, sec = 8, 0, 0, 0.0
+    while sec < budget_s:
+        rt = np.sort(rng.integers(0, w.T, size=n)).astype(np.int32)
+        rb = np.zeros(n, np.int32)
+        idx = torch.as_tensor(rt, device=x["k"].device).long()
+        q = {key: x[key][0, idx].float().cpu().numpy() for key in ("q_signal", "q_noise", "lam", "gate")}
+        t0 = time.perf_counter()
+        oracle.prefill_rows(k, v, q["q_signal"], q["q_noise"], q["lam"], q["gate"], rb, rt, window=w.window,
+                            lib=lib)
+        sec += time.perf_counter() - t0
+        rows += n
+        vis = rt.astype(np.int64) + 1
+        if w.window > 0:
+            vis = np.minimum(vis, w.window)
+        pairs += int(vis.sum())
+        n *= 2
+    tflops = pairs * N_HEADS * FLOP_PER_PAIR / sec / 1e12
+    total = pairs_prefill(w.B, w.T, w.window) * N_HEADS * FLOP_PER_PAIR
+    model, ncpu = cpu_info()
+    return {"value": tflops, "unit": "TFLOP/s", "cores": oracle.num_threads(lib), "kind": "oracle",
+            "arithmetic": "fp32 (the oracle's source built with fp32 sums and expf)",
+            "sample": "%d random query rows (all 80 heads) of the %s workload, %.1f s of compute; "
+                      "extrapolated to the whole launch by unmasked pairs" % (rows, w.name, sec),
+            "extrapolated_s_per_step": total / (tflops * 1e12),
+            "cpu_model": model, "host_cpus": ncpu}
+
+
+def cpu_baseline_configs(full=False):
+    """The fp32 oracle in full on whole workloads: the tiny config (all threads
+    and one thread) and the 128-key window decode; with full=True also the 4K
+    prefill, the 32K window prefill and the full-causal decode."""
     import numpy as np
     import torch
     import oracle
     import workload as W
-    w = W.WORKLOADS["pf_full_4k"]
-    x = W.prefill_inputs(w, seed=0, device="cpu")
-    f = {k: v.float().numpy() for k, v in x.items()}
-    rng = np.random.default_rng(0)
-    n, done_rows, done_pairs, elapsed = 32, 0, 0, 0.0
-    while elapsed < budget_s:
-        rt = rng.integers(0, w.T, size=n).astype(np.int32)
-        rb = np.zeros(n, np.int32)
+    lib = oracle.library_fp32()
+    threads = oracle.num_threads(lib)
+    res = {}
+
+    def f32(t):
+        return t.float().cpu().numpy()
+
+    def prefill_full(name, n_threads=None):
+        w = W.WORKLOADS[name]
+        x = W.prefill_inputs(w, seed=0, device="cuda")
+        a = {k: f32(t) for k, t in x.items()}
+        del x
+        torch.cuda.empty_cache()
+        if n_threads:
+            oracle.set_threads(n_threads, lib)
         t0 = time.perf_counter()
-        oracle.prefill_rows(f["k"], f["v"], f["q_signal"][0, rt], f["q_noise"][0, rt], f["lam"][0, rt],
-                            f["gate"][0, rt], rb, rt, window=0)
-        elapsed += time.perf_counter() - t0
-        done_rows += n
-        done_pairs += int((rt.astype(np.int64) + 1).sum())
-        n *= 2
-    tflops = done_pairs * N_HEADS * FLOP_PER_PAIR / elapsed / 1e12
-    return {"value": tflops, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": "%d random query rows (all 80 heads) of the B=1 T=4096 full-causal prefill, "
-                      "%.1f s of CPU time, fp64 oracle" % (done_rows, elapsed)}
+        oracle.prefill(a["q_signal"], a["q_noise"], a["k"], a["v"], a["lam"], a["gate"], window=w.window, lib=lib)
+        sec = time.perf_counter() - t0
+        oracle.set_threads(threads, lib)
+        flops = pairs_prefill(w.B, w.T, w.window) * (w.n_sig + w.n_kv) * FLOP_PER_PAIR
+        return {"seconds": sec, "tflops": flops / sec / 1e12, "threads": n_threads or threads}
+
+    def decode_full(name):
+        w = W.WORKLOADS[name]
+        d = W.decode_inputs(w, seed=0, device="cuda")
+        cu = d["cu_seqlens"].cpu().numpy().astype(np.int64)
+        lengths = d["lengths"].tolist()
+        vis = [min(L, w.window) if w.window > 0 else L for L in lengths]
+        # the rows each query sees, packed (positions do not enter the scores)
+        keep = torch.cat([torch.arange(int(cu[b + 1]) - vis[b], int(cu[b + 1])) for b in range(w.B)])
+        kc = np.empty((len(keep),) + tuple(d["k_cache"].shape[1:]), np.float32)
+        vc = np.empty((len(keep),) + tuple(d["v_cache"].shape[1:]), np.float32)
+        step = 1 << 18
+        for i in range(0, len(keep), step):
+            sel = keep[i:i + step].to("cuda")
+            kc[i:i + step] = f32(d["k_cache"][sel])
+            vc[i:i + step] = f32(d["v_cache"][sel])
+        cu_v = np.concatenate([[0], np.cumsum(vis)]).astype(np.int32)
+        q = {k: f32(d[k]) for k in ("q_signal", "q_noise", "lam", "gate")}
+        del d
+        torch.cuda.empty_cache()
+        t0 = time.perf_counter()
+        oracle.decode(q["q_signal"], q["q_noise"], kc, vc, cu_v, q["lam"], q["gate"], window=0, lib=lib)
+        sec = time.perf_counter() - t0
+        nbytes = decode_bytes(lengths, w.window)
+        flops = sum(vis) * N_HEADS * FLOP_PER_PAIR
+        return {"seconds": sec, "gbs": nbytes / sec / 1e9, "tflops": flops / sec / 1e12, "threads": threads}
+
+    res["tiny"] = prefill_full("tiny")
+    res["tiny_1_thread"] = prefill_full("tiny", n_threads=1)
+    res["dec_swa"] = decode_full("dec_swa")
+    if full:
+        res["pf_full_4k"] = prefill_full("pf_full_4k")
+        res["pf_swa_32k"] = prefill_full("pf_swa_32k")
+        res["dec_full"] = decode_full("dec_full")
+    return res
 
 
-def load_traffic(name):
-    """HBM bytes per launch from committed rocprofv3 counter runs, if they
-    were taken on the current kernel sources."""
-    p = os.path.join(ROOT, "profiles", "traffic_%s.json" % name)
-    if not os.path.exists(p):
-        return None
-    t = json.load(open(p))
-    if t.get("source_hash") != source_hash():
-        return None
-    return t.get("bytes_per_launch")
-
-
-def bench_prefill(name, steps, warmup):
+def bench_prefill(name, steps, warmup, settle_s=0.0, keep_inputs=False):
     import torch
     import attention_gdla_prefill_amd as gdla
     import workload as W
@@ -197,14 +361,20 @@ def bench_prefill(name, steps, warmup):
         out = torch.empty((w.B, w.T - P, w.n_sig, 128), dtype=torch.bfloat16, device="cuda")
         fn = lambda: gdla.prefill_prefix(x["q_signal"], x["q_noise"], x["k"], x["v"], x["lam"],
                                          x["gate"], window=w.window, out=out)
-    wall, ev = time_kernel(fn, steps, warmup, stream)
+    wall, ev, settle = time_kernel(fn, steps, warmup, stream, settle_s)
     kern_ms = sum(ev) / len(ev)
     flops = pairs_prefill(w.B, w.T, w.window, P) * N_HEADS * FLOP_PER_PAIR
     nbytes = prefill_bytes(w.B, w.T, prefix=P)
-    del x, out
-    torch.cuda.empty_cache()
-    return {"wall_ms": wall, "kernel_ms": kern_ms, "flops": flops, "bytes": nbytes,
-            "tflops": flops / (kern_ms * 1e-3) / 1e12, "gbs": nbytes / (kern_ms * 1e-3) / 1e9}
+    del out
+    res = {"wall_ms": wall, "kernel_ms": kern_ms, "kernel_ms_min": min(ev), "kernel_ms_max": max(ev),
+           "flops": flops, "bytes": nbytes, "settle": settle,
+           "tflops": flops / (kern_ms * 1e-3) / 1e12, "gbs": nbytes / (kern_ms * 1e-3) / 1e9}
+    if keep_inputs:
+        res["inputs"] = x
+    else:
+        del x
+        torch.cuda.empty_cache()
+    return res
 
 
 def prep_bytes(w, d_model=4096):
@@ -230,29 +400,15 @@ def bench_prep(name, steps, warmup):
     d = W.prep_inputs(w, seed=0, device="cuda")
     lam = torch.empty((w.B, w.T, w.n_sig), dtype=torch.bfloat16, device="cuda")
     gate = torch.empty_like(d["gate_pre"])
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
-    stream = torch.cuda.current_stream()
     call = lambda: gdla.prep(d["q_signal"], d["q_noise"], d["k_rope"], d["k"], d["x"], d["w_lambda"],
                              d["gate_pre"], lam_out=lam, gate_out=gate)
-    for _ in range(warmup):
-        call()
-    torch.cuda.synchronize()
-    times = []
-    for _ in range(steps):
-        flush.fill_(1)
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        call()
-        b.record(stream)
-        torch.cuda.synchronize()
-        times.append(a.elapsed_time(b))
-    ms = sorted(times)[len(times) // 2]
+    ms, ms_dirty = cold_times(call, steps, warmup)
     nbytes = prep_bytes(w)
-    del d, lam, gate, flush
+    del d, lam, gate
     torch.cuda.empty_cache()
     return {"kernel_ms": ms, "bytes": nbytes, "gbs": nbytes / (ms * 1e-3) / 1e9,
-            "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
-            "cache": "cold (512 MB buffer rewritten before each launch)"}
+            "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, "cache": COLD,
+            "kernel_ms_dirty_flush": ms_dirty}
 
 
 def bench_backward(name, steps, warmup):
@@ -273,7 +429,7 @@ def bench_backward(name, steps, warmup):
     stream = torch.cuda.current_stream()
     fn = lambda: gdla.prefill_backward(x["q_signal"], x["q_noise"], x["k"], x["v"], x["lam"], x["gate"], d_out,
                                        window=w.window, workspace=ws)
-    wall, ev = time_kernel(fn, steps, warmup, stream)
+    wall, ev, _ = time_kernel(fn, steps, warmup, stream)
     ms = sum(ev) / len(ev)
     pairs = pairs_prefill(w.B, w.T, w.window, 0) * (w.n_sig + w.n_kv)
     del x, d_out, ws
@@ -294,31 +450,16 @@ def bench_decode(name, steps, warmup):
     out = torch.empty((w.B, w.n_sig, 128), dtype=torch.bfloat16, device="cuda")
     ws = torch.empty(max(16, gdla.decode_workspace_size(w.B, w.n_kv, max_len, w.window)),
                      dtype=torch.uint8, device="cuda")
-    # a buffer larger than the 256 MB Infinity Cache, rewritten before each launch
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
-    stream = torch.cuda.current_stream()
     call = lambda: gdla.decode(d["q_signal"], d["q_noise"], d["k_cache"], d["v_cache"],
                                d["cu_seqlens"], max_len, d["lam"], d["gate"], window=w.window,
                                out=out, workspace=ws)
-    for _ in range(warmup):
-        call()
-    torch.cuda.synchronize()
-    times = []
-    for _ in range(steps):
-        flush.fill_(1)
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        call()
-        b.record(stream)
-        torch.cuda.synchronize()
-        times.append(a.elapsed_time(b))
-    kern_ms = sorted(times)[len(times) // 2]
+    kern_ms, ms_dirty = cold_times(call, steps, warmup)
     nbytes = decode_bytes(lengths, w.window)
-    del d, out, ws, flush
+    del d, out, ws
     torch.cuda.empty_cache()
     return {"kernel_ms": kern_ms, "bytes": nbytes, "gbs": nbytes / (kern_ms * 1e-3) / 1e9,
-            "hbm_frac": nbytes / (kern_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
-            "cache": "cold (512 MB buffer rewritten before each launch)"}
+            "hbm_frac": nbytes / (kern_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, "cache": COLD,
+            "kernel_ms_dirty_flush": ms_dirty}
 
 
 def measured_peaks():
@@ -368,49 +509,51 @@ def bench_decode_latent(name, steps, warmup):
     out = torch.empty((w.B, w.n_sig, 128), dtype=torch.bfloat16, device="cuda")
     ws = torch.empty(gdla.decode_latent_workspace_size(w.B, w.n_kv, max_len, w.window),
                      dtype=torch.uint8, device="cuda")
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
-    stream = torch.cuda.current_stream()
     call = lambda: gdla.decode_latent(d["q_signal"], d["q_noise"], d["latent"], d["cu_seqlens"], max_len,
                                       d["w_uk"], d["w_uv"], d["lam"], d["gate"], window=w.window,
                                       out=out, workspace=ws)
-    for _ in range(warmup):
-        call()
-    torch.cuda.synchronize()
-    times = []
-    for _ in range(steps):
-        flush.fill_(1)
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        call()
-        b.record(stream)
-        torch.cuda.synchronize()
-        times.append(a.elapsed_time(b))
-    kern_ms = sorted(times)[len(times) // 2]
+    kern_ms, ms_dirty = cold_times(call, steps, warmup)
     nbytes = decode_latent_bytes(lengths, w.window)
     expanded = decode_bytes(lengths, w.window)
-    del d, out, ws, flush
+    del d, out, ws
     torch.cuda.empty_cache()
     return {"kernel_ms": kern_ms, "bytes": nbytes, "gbs": nbytes / (kern_ms * 1e-3) / 1e9,
             "hbm_frac": nbytes / (kern_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
-            "expanded_equivalent_gbs": expanded / (kern_ms * 1e-3) / 1e9,
-            "cache": "cold (512 MB buffer rewritten before each launch)"}
+            "expanded_equivalent_gbs": expanded / (kern_ms * 1e-3) / 1e9, "cache": COLD,
+            "kernel_ms_dirty_flush": ms_dirty}
+
+
+PREFILL_WORKLOADS = ("pf_full_128k", "pf_full_4k", "pf_swa_32k", "pf_prefix_4k_32k", "pf_swa_rank")
+EXTRA_NAMES = ("pf_full_4k", "pf_swa_32k", "pf_full_128k", "pf_prefix_4k_32k", "pf_swa_rank", "dec_swa",
+               "dec_latent_full", "dec_latent_swa", "prep_4k", "prep_swa_32k", "bwd_4k")
+
+
+def decode_roofline(r, name):
+    traffic = load_traffic(name)
+    return {"bound": "hbm", "achieved": r["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": r["gbs"] / PEAK_HBM_GBS, "traffic": traffic, "workload": name,
+            "kernel": " + ".join(traffic_kernels(name)), "kernel_ms": r["kernel_ms"],
+            "kernel_ms_dirty_flush": r["kernel_ms_dirty_flush"],
+            "algorithmic_bytes_per_launch": r["bytes"], "cache": r["cache"]}
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    # the GPU's clock needs ~0.1 s of steady work to settle: the default
-    # warmup covers that (about 0.1 s at 4K) before 100 timed steps
-    ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=200)
-    ap.add_argument("--workload", default="pf_full_4k",
-                    choices=["pf_full_4k", "pf_swa_32k", "pf_full_128k", "pf_prefix_4k_32k", "pf_swa_rank"])
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--settle-s", type=float, default=0.5,
+                    help="untimed steady work before the timed steps, in seconds (with at least "
+                         "--warmup launches): the GPU clock needs ~0.1 s of load to settle")
+    ap.add_argument("--workload", default="pf_full_128k", choices=PREFILL_WORKLOADS + ("dec_full", "dec_swa"))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-full", action="store_true",
+                    help="also time the fp32 oracle in full on the 4K prefill, the 32K window prefill "
+                         "and the full-causal decode (about a minute of CPU)")
+    ap.add_argument("--no-decode", action="store_true", help="skip the full-causal decode roofline")
     ap.add_argument("--no-extra", action="store_true")
-    ap.add_argument("--extras", default="pf_swa_32k,pf_full_128k,pf_prefix_4k_32k,pf_swa_rank,"
-                                        "dec_full,dec_swa,dec_latent_full,dec_latent_swa,prep_4k,prep_swa_32k,bwd_4k",
-                    help="comma-separated extra workloads to time (a profile of one workload "
-                         "names just that one)")
+    ap.add_argument("--extras", default=",".join(EXTRA_NAMES),
+                    help="comma-separated extra workloads to time (a profile of one workload names just that one)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run one 1 GiB device copy (reference for HBM counter scaling)")
     ap.add_argument("--peaks", action="store_true",
@@ -429,8 +572,7 @@ def main():
         sys.exit(2)
     wanted = [] if args.no_extra else [x for x in args.extras.split(",") if x]
     for name in wanted:
-        if name not in ("pf_swa_32k", "pf_full_128k", "pf_prefix_4k_32k", "pf_swa_rank", "dec_full",
-                        "dec_swa", "dec_latent_full", "dec_latent_swa", "prep_4k", "prep_swa_32k", "bwd_4k"):
+        if name not in EXTRA_NAMES:
             print("unknown extra workload %r" % name, file=sys.stderr)
             sys.exit(2)
 
@@ -443,9 +585,21 @@ def main():
     L.load()          # fails loudly if the HIP library is missing
 
     w = W.WORKLOADS[args.workload]
-    print("[bench] %s steps=%d warmup=%d" % (args.workload, args.steps, args.warmup),
+    print("[bench] %s steps=%d warmup=%d settle=%.2fs" % (args.workload, args.steps, args.warmup, args.settle_s),
           file=sys.stderr, flush=True)
-    main_res = bench_prefill(args.workload, args.steps, args.warmup)
+    decode_main = args.workload.startswith("dec_")
+    cpu = None
+    if decode_main:
+        main_res = bench_decode(args.workload, args.steps, args.warmup)
+    else:
+        main_res = bench_prefill(args.workload, args.steps, args.warmup, args.settle_s,
+                                 keep_inputs=not args.no_cpu_baseline)
+        if not args.no_cpu_baseline:
+            print("[bench] cpu baseline (fp32 oracle, sampled rows of %s)" % args.workload, file=sys.stderr,
+                  flush=True)
+            cpu = cpu_baseline_headline(main_res["inputs"], w)
+            del main_res["inputs"]
+            torch.cuda.empty_cache()
 
     if args.copy_probe:
         a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
@@ -454,62 +608,92 @@ def main():
         torch.cuda.synchronize()
         del a, b
 
+    dec_roof = None
+    if not args.no_decode and not decode_main:
+        print("[bench] decode roofline dec_full", file=sys.stderr, flush=True)
+        dec_roof = decode_roofline(bench_decode("dec_full", 10, 2), "dec_full")
+
     extra = {}
-    if wanted:
-        for name in ("pf_swa_32k", "pf_full_128k", "pf_prefix_4k_32k", "pf_swa_rank"):
-            if name == args.workload or name not in wanted:
-                continue
-            print("[bench] extra %s" % name, file=sys.stderr, flush=True)
-            steps, warm = (3, 1) if name == "pf_full_128k" else (50, 50)
-            r = bench_prefill(name, steps, warm)
-            extra[name] = {"tflops": r["tflops"], "mfma_frac": r["tflops"] / PEAK_BF16_TFLOPS,
-                           "gbs": r["gbs"], "hbm_frac": r["gbs"] / PEAK_HBM_GBS,
-                           "kernel_ms": r["kernel_ms"], "steps": steps}
-        for name in ("dec_full", "dec_swa", "dec_latent_full", "dec_latent_swa"):
-            if name not in wanted:
-                continue
-            print("[bench] extra %s" % name, file=sys.stderr, flush=True)
-            fn = bench_decode_latent if name.startswith("dec_latent") else bench_decode
-            extra[name] = fn(name, 10, 2)
-        for name, shape in (("prep_4k", "pf_full_4k"), ("prep_swa_32k", "pf_swa_32k")):
-            if name not in wanted:
-                continue
-            print("[bench] extra %s" % name, file=sys.stderr, flush=True)
-            extra[name] = dict(bench_prep(shape, 20, 5), shapes=shape)
-        if "bwd_4k" in wanted:
-            print("[bench] extra bwd_4k", file=sys.stderr, flush=True)
-            extra["bwd_4k"] = dict(bench_backward("pf_full_4k", 20, 10), shapes="pf_full_4k")
+    for name in ("pf_full_4k", "pf_swa_32k", "pf_full_128k", "pf_prefix_4k_32k", "pf_swa_rank"):
+        if name == args.workload or name not in wanted:
+            continue
+        print("[bench] extra %s" % name, file=sys.stderr, flush=True)
+        steps, warm = (3, 1) if name == "pf_full_128k" else (50, 10)
+        r = bench_prefill(name, steps, warm, args.settle_s)
+        extra[name] = {"tflops": r["tflops"], "mfma_frac": r["tflops"] / PEAK_BF16_TFLOPS,
+                       "gbs": r["gbs"], "hbm_frac": r["gbs"] / PEAK_HBM_GBS, "kernel_ms": r["kernel_ms"],
+                       "steps": steps, "settle": r["settle"], "traffic": load_traffic(name)}
+    for name in ("dec_swa", "dec_latent_full", "dec_latent_swa"):
+        if name == args.workload or name not in wanted:
+            continue
+        print("[bench] extra %s" % name, file=sys.stderr, flush=True)
+        fn = bench_decode_latent if name.startswith("dec_latent") else bench_decode
+        extra[name] = fn(name, 10, 2)
+        if name == "dec_swa":
+            extra[name]["traffic"] = load_traffic(name)
+    for name, shape in (("prep_4k", "pf_full_4k"), ("prep_swa_32k", "pf_swa_32k")):
+        if name not in wanted:
+            continue
+        print("[bench] extra %s" % name, file=sys.stderr, flush=True)
+        extra[name] = dict(bench_prep(shape, 20, 5), shapes=shape)
+    if "bwd_4k" in wanted:
+        print("[bench] extra bwd_4k", file=sys.stderr, flush=True)
+        extra["bwd_4k"] = dict(bench_backward("pf_full_4k", 20, 10), shapes="pf_full_4k")
 
     peaks = measured_peaks() if args.peaks else None
 
-    cpu = None
     if not args.no_cpu_baseline:
-        print("[bench] cpu baseline", file=sys.stderr, flush=True)
-        cpu = cpu_baseline()
+        print("[bench] cpu baseline: whole small configs%s" % (" and --cpu-full" if args.cpu_full else ""),
+              file=sys.stderr, flush=True)
+        configs = cpu_baseline_configs(full=args.cpu_full)
+        if cpu is None:
+            import oracle
+            model, ncpu = cpu_info()
+            cpu = {"value": configs["dec_swa"]["gbs"], "unit": "GB/s", "kind": "oracle",
+                   "cores": oracle.num_threads(oracle.library_fp32()),
+                   "sample": "the whole dec_swa workload", "cpu_model": model, "host_cpus": ncpu}
+        cpu["configs"] = configs
 
-    traffic = load_traffic(args.workload)
+    if decode_main:
+        value, unit = main_res["gbs"], "GB/s"
+        roof = decode_roofline(main_res, args.workload)
+        ms_per_step = main_res["kernel_ms"]
+        config = {"workload": "%s: decode, %d sequences, cached lengths U{%d..%d}, %d KV / %d signal / %d noise "
+                              "heads, qk 192 / v 128, %s, cold cache"
+                              % (w.name, w.B, w.len_lo, w.len_hi, w.n_kv, w.n_sig, w.n_kv,
+                                 "full causal" if w.window == 0 else "window %d" % w.window),
+                  "global_batch": w.B, "parallelism": "single GPU"}
+    else:
+        value, unit = main_res["flops"] / (main_res["wall_ms"] * 1e-3) / 1e12, "TFLOP/s"
+        ms_per_step = main_res["wall_ms"]
+        roof = {"bound": "mfma", "achieved": main_res["tflops"], "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": main_res["tflops"] / PEAK_BF16_TFLOPS,
+                "traffic": load_traffic(args.workload), "kernel": "prefill_kernel",
+                "kernel_ms": main_res["kernel_ms"], "kernel_ms_min": main_res["kernel_ms_min"],
+                "kernel_ms_max": main_res["kernel_ms_max"], "flops_per_launch": main_res["flops"],
+                "algorithmic_bytes_per_launch": main_res["bytes"],
+                "hbm_frac_algorithmic": main_res["gbs"] / PEAK_HBM_GBS}
+        config = {"workload": "%s: prefill B=%d T=%d, %d KV / %d signal / %d noise heads, qk 192 / v 128, %s"
+                              % (w.name, w.B, w.T, w.n_kv, w.n_sig, w.n_kv,
+                                 "full causal" if w.window == 0 else "window %d" % w.window),
+                  "global_batch": w.B, "seq_len": w.T, "parallelism": "single GPU"}
     line = {
         "metric": METRIC,
-        "value": main_res["flops"] / (main_res["wall_ms"] * 1e-3) / 1e12,
-        "unit": "TFLOP/s",
+        "value": value,
+        "unit": unit,
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": main_res["wall_ms"],
+        "settle": main_res.get("settle"),
+        "ms_per_step": ms_per_step,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "%s: prefill B=%d T=%d, %d KV / %d signal / %d noise heads, qk 192 / "
-                               "v 128, %s" % (w.name, w.B, w.T, w.n_kv, w.n_sig, w.n_kv,
-                                              "full causal" if w.window == 0 else "window %d" % w.window),
-                   "global_batch": w.B, "seq_len": w.T, "parallelism": "single GPU"},
-        "roofline": {"bound": "mfma", "achieved": main_res["tflops"], "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": main_res["tflops"] / PEAK_BF16_TFLOPS,
-                     "traffic": traffic, "kernel": "prefill_kernel",
-                     "kernel_ms": main_res["kernel_ms"], "flops_per_launch": main_res["flops"],
-                     "algorithmic_bytes_per_launch": main_res["bytes"]},
+        "config": config,
+        "roofline": roof,
+        "decode_roofline": dec_roof,
         "cpu_baseline": cpu,
         "extra": extra,
     }
