@@ -67,3 +67,16 @@ def status_string(status):
 def check(status):
     if status != 0:
         raise GdlaError(status, load().gdla_last_error().decode())
+
+
+def sync_check_enabled():
+    """GDLA_SYNC_CHECK set to anything but "" or "0"."""
+    return os.environ.get("GDLA_SYNC_CHECK", "") not in ("", "0")
+
+
+def after_launch(device):
+    """Called after every launch: with GDLA_SYNC_CHECK=1 it waits for the
+    device, which raises any asynchronous HIP error there and then."""
+    if sync_check_enabled():
+        import torch
+        torch.cuda.synchronize(device)

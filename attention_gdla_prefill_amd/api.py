@@ -3,6 +3,10 @@
 Every step of the computation runs in the HIP kernels behind include/gdla.h;
 these functions check tensor metadata, pick the current HIP stream and call
 the C ABI through ctypes.  Tensors are torch bf16 tensors on a ROCm device.
+
+With the environment variable GDLA_SYNC_CHECK=1 every call waits for its
+kernels before returning, so that an asynchronous HIP error (a fault inside
+a kernel) is raised by the call that caused it rather than by a later one.
 """
 import ctypes
 import math
@@ -57,6 +61,7 @@ def prefill(q_signal, q_noise, k, v, lam, gate, window=0, scale=None, out=None):
         q_signal.data_ptr(), q_noise.data_ptr(), k.data_ptr(), v.data_ptr(), lam.data_ptr(),
         gate.data_ptr(), out.data_ptr(), B, T, n_kv, GROUP, D_QK, D_V, int(window),
         float(scale), _stream_ptr(k.device)))
+    _lib.after_launch(k.device)
     return out
 
 
@@ -90,6 +95,7 @@ def prefill_prefix(q_signal, q_noise, k, v, lam, gate, window=0, scale=None, out
         q_signal.data_ptr(), q_noise.data_ptr(), k.data_ptr(), v.data_ptr(), lam.data_ptr(),
         gate.data_ptr(), out.data_ptr(), B, Tq, P, n_kv, GROUP, D_QK, D_V, int(window),
         float(scale), _stream_ptr(k.device)))
+    _lib.after_launch(k.device)
     return out
 
 
@@ -131,6 +137,7 @@ def decode(q_signal, q_noise, k_cache, v_cache, cu_seqlens, max_seqlen_k, lam, g
         cu_seqlens.data_ptr(), int(max_seqlen_k), lam.data_ptr(), gate.data_ptr(),
         out.data_ptr(), workspace.data_ptr(), workspace.numel(), B, n_kv, GROUP, D_QK, D_V,
         int(window), float(scale), _stream_ptr(k_cache.device)))
+    _lib.after_launch(k_cache.device)
     return out
 
 
@@ -178,6 +185,7 @@ def decode_latent(q_signal, q_noise, latent_cache, cu_seqlens, max_seqlen_k, w_u
         int(max_seqlen_k), w_uk.data_ptr(), w_uv.data_ptr(), lam.data_ptr(), gate.data_ptr(),
         out.data_ptr(), workspace.data_ptr(), workspace.numel(), B, n_kv, GROUP, D_C, D_R, D_V,
         int(window), float(scale), _stream_ptr(latent_cache.device)))
+    _lib.after_launch(latent_cache.device)
     return out
 
 
@@ -214,6 +222,7 @@ def prep(q_signal, q_noise, k_rope, k, x, w_lambda, gate_pre, pos0=0, rope_theta
         q_signal.data_ptr(), q_noise.data_ptr(), k_rope.data_ptr(), k.data_ptr(), x.data_ptr(),
         w_lambda.data_ptr(), lam_out.data_ptr(), gate_pre.data_ptr(), gate_out.data_ptr(), B, T, n_kv,
         GROUP, D_QK, D_V, d_model, int(pos0), float(rope_theta), _stream_ptr(k.device)))
+    _lib.after_launch(k.device)
     return lam_out, gate_out
 
 
@@ -250,4 +259,5 @@ def prefill_backward(q_signal, q_noise, k, v, lam, gate, d_out, window=0, scale=
         d_out.data_ptr(), grads["q_signal"].data_ptr(), grads["q_noise"].data_ptr(), grads["k"].data_ptr(),
         grads["v"].data_ptr(), grads["lam"].data_ptr(), grads["gate"].data_ptr(), workspace.data_ptr(),
         workspace.numel(), B, T, n_kv, GROUP, D_QK, D_V, int(window), float(scale), _stream_ptr(k.device)))
+    _lib.after_launch(k.device)
     return grads
