@@ -16,8 +16,6 @@ from test_oracle_pins import (D_QK, brute_force, golden_expected, golden_inputs,
 
 @pytest.fixture(scope="module")
 def lib32():
-    from oracle import build
-    build.build_oracle(fp32=True)
     return oracle.library_fp32()
 
 
