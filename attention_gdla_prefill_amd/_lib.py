@@ -22,6 +22,9 @@ SIGNATURES = {
     "gdla_decode_workspace_size": (ctypes.c_size_t, [_I, _I, _I, _I]),
     "gdla_decode": (_I, [_P, _P, _P, _P, _P, _I, _P, _P, _P, _P, ctypes.c_size_t,
                          _I, _I, _I, _I, _I, _I, ctypes.c_float, _P]),
+    "gdla_decode_noalloc_max_scratch": (ctypes.c_size_t, []),
+    "gdla_decode_noalloc": (_I, [_P, _P, _P, _P, _P, _I, _P, _P, _P, _I, _I, _I, _I, _I, _I,
+                                 ctypes.c_float, _P]),
     "gdla_decode_latent_workspace_size": (ctypes.c_size_t, [_I, _I, _I, _I]),
     "gdla_decode_latent": (_I, [_P, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P, ctypes.c_size_t,
                                 _I, _I, _I, _I, _I, _I, _I, ctypes.c_float, _P]),

@@ -141,6 +141,40 @@ def decode(q_signal, q_noise, k_cache, v_cache, cu_seqlens, max_seqlen_k, lam, g
     return out
 
 
+def decode_noalloc_max_scratch():
+    """Bytes of the library's per-GPU scratch that decode_noalloc uses."""
+    return int(_lib.load().gdla_decode_noalloc_max_scratch())
+
+
+def decode_noalloc(q_signal, q_noise, k_cache, v_cache, cu_seqlens, max_seqlen_k, lam, gate,
+                   window=0, scale=None, out=None):
+    """decode() without a workspace: the split partials go to the library's
+    own per-GPU scratch (gdla_decode_noalloc).  With `out` given the call
+    allocates nothing; calls on one GPU must be ordered on one stream."""
+    total, n_kv, _ = k_cache.shape
+    B = q_signal.shape[0]
+    n_sig = n_kv * GROUP
+    _check(q_signal, "q_signal", (B, n_sig, D_QK))
+    _check(q_noise, "q_noise", (B, n_kv, D_QK))
+    _check(k_cache, "k_cache", (total, n_kv, D_QK))
+    _check(v_cache, "v_cache", (total, n_kv, D_V))
+    _check(cu_seqlens, "cu_seqlens", (B + 1,), dtype=torch.int32)
+    _check(lam, "lam", (B, n_sig))
+    _check(gate, "gate", (B, n_sig, D_V))
+    if out is None:
+        out = torch.empty((B, n_sig, D_V), dtype=torch.bfloat16, device=k_cache.device)
+    _check(out, "out", (B, n_sig, D_V))
+    if scale is None:
+        scale = 1.0 / math.sqrt(D_QK)
+    lib = _lib.load()
+    _lib.check(lib.gdla_decode_noalloc(
+        q_signal.data_ptr(), q_noise.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+        cu_seqlens.data_ptr(), int(max_seqlen_k), lam.data_ptr(), gate.data_ptr(),
+        out.data_ptr(), B, n_kv, GROUP, D_QK, D_V, int(window), float(scale), _stream_ptr(k_cache.device)))
+    _lib.after_launch(k_cache.device)
+    return out
+
+
 D_C, D_R = 512, 64
 
 

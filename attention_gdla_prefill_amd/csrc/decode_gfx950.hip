@@ -25,6 +25,7 @@
 #include "gdla_launch.h"
 
 #include <algorithm>
+#include <mutex>
 
 namespace gdla {
 
@@ -517,6 +518,42 @@ hipError_t launch_decode(const void *qs, const void *qn, const void *kc, const v
     if (e != hipSuccess || n_split == 1) return e;
     hipLaunchKernelGGL(decode_combine_kernel, dim3(n_kv, B), dim3(D_V), 0, stream, p);
     return hipGetLastError();
+}
+
+// ---- scratch for callers that cannot allocate (gdla_decode_noalloc) -------
+//
+// The split partials of gdla_decode_noalloc live in this file-scope device
+// array instead of a caller workspace.  Each GPU the library runs on holds its
+// own copy until the process ends.  In host code `scratch` names a host-side
+// stand-in, not the device array: its device address is looked up once per
+// device with hipGetSymbolAddress (with that device current) and only that
+// address is passed to the kernels.  Every call on one GPU shares the array,
+// so calls that overlap on one GPU (different streams, no ordering) race.
+// Nothing in it needs to start at zero: every split writes its whole partial
+// before the combine reads it.
+static __device__ __align__(256) unsigned char scratch[DECODE_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int MAX_DEVICES = 64;
+std::mutex scratch_mutex;
+void *scratch_ptr[MAX_DEVICES];
+}  // namespace
+
+hipError_t decode_noalloc_scratch(void **ptr) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= MAX_DEVICES) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(scratch_mutex);
+    if (!scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        scratch_ptr[dev] = p;
+    }
+    *ptr = scratch_ptr[dev];
+    return hipSuccess;
 }
 
 }  // namespace gdla

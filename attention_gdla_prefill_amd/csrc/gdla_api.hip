@@ -131,9 +131,10 @@ extern "C" size_t gdla_decode_workspace_size(int B, int n_kv, int max_seqlen_k, 
 
 namespace {
 
-// Checks of gdla_decode's arguments.  `workspace` is the area the split
-// partials go to; with `own_workspace` false its size and alignment are the
-// caller's to check.  Returns the status; on GDLA_OK, n_split and need are set.
+// Checks shared by gdla_decode and gdla_decode_noalloc.  `workspace` is the
+// area the split partials go to (the caller's, or the library's scratch);
+// with `own_workspace` false its size and alignment are the caller's to
+// check.  Returns the status; on GDLA_OK, n_split and need are set.
 int check_decode(const void *q_signal, const void *q_noise, const void *k_cache, const void *v_cache,
                  const int32_t *cu_seqlens_k, int max_seqlen_k, const void *lambda_, const void *gate,
                  const void *out, const void *workspace, size_t workspace_bytes, bool own_workspace, int B,
@@ -202,6 +203,39 @@ extern "C" int gdla_decode(const void *q_signal, const void *q_noise, const void
     if (B == 0) return GDLA_OK;
     hipError_t e = gdla::launch_decode(q_signal, q_noise, k_cache, v_cache, cu_seqlens_k, lambda_,
                                        gate, out, workspace, B, n_kv, n_split, window, softmax_scale,
+                                       static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(GDLA_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
+    return GDLA_OK;
+}
+
+extern "C" size_t gdla_decode_noalloc_max_scratch(void) { return gdla::DECODE_NOALLOC_SCRATCH_BYTES; }
+
+extern "C" int gdla_decode_noalloc(const void *q_signal, const void *q_noise, const void *k_cache,
+                                   const void *v_cache, const int32_t *cu_seqlens_k, int max_seqlen_k,
+                                   const void *lambda_, const void *gate, void *out, int B, int n_kv, int group,
+                                   int d_qk, int d_v, int window, float softmax_scale, void *stream) {
+    g_last_error[0] = 0;
+    int n_split = 1;
+    size_t need = 0;
+    if (int rc = check_decode(q_signal, q_noise, k_cache, v_cache, cu_seqlens_k, max_seqlen_k, lambda_, gate, out,
+                              nullptr, 0, false, B, n_kv, group, d_qk, d_v, window, softmax_scale, n_split, need))
+        return rc;
+    if (B == 0) return GDLA_OK;
+    if (need > gdla::DECODE_NOALLOC_SCRATCH_BYTES)
+        return fail(GDLA_ERR_WORKSPACE,
+                    "the split partials need %zu bytes, more than the %zu-byte scratch of gdla_decode_noalloc "
+                    "(use gdla_decode with a workspace, or fewer sequences or KV heads per call)",
+                    need, gdla::DECODE_NOALLOC_SCRATCH_BYTES);
+    void *scratch = nullptr;
+    if (need > 0) {
+        hipError_t e = gdla::decode_noalloc_scratch(&scratch);
+        if (e != hipSuccess) return fail(GDLA_ERR_HIP, "decode scratch lookup: %s", hipGetErrorString(e));
+        const Range w = {"scratch", (uintptr_t)scratch, (uintptr_t)scratch + need};
+        const Range o = {"out", (uintptr_t)out, (uintptr_t)out + (uintptr_t)B * n_kv * group * d_v * 2};
+        if (overlaps(o, w)) return fail(GDLA_ERR_INVALID_ARG, "out overlaps the library's scratch");
+    }
+    hipError_t e = gdla::launch_decode(q_signal, q_noise, k_cache, v_cache, cu_seqlens_k, lambda_,
+                                       gate, out, scratch, B, n_kv, n_split, window, softmax_scale,
                                        static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(GDLA_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
     return GDLA_OK;

@@ -29,6 +29,12 @@ hipError_t launch_decode(const void *qs, const void *qn, const void *kc, const v
                          void *workspace, int B, int n_kv, int n_split, int window, float scale,
                          hipStream_t stream);
 
+// Largest split-partials area gdla_decode_noalloc can hold (its device
+// scratch array), and the current device's address of that array (looked up
+// on the first call on each device).
+constexpr size_t DECODE_NOALLOC_SCRATCH_BYTES = (size_t)96 << 20;
+hipError_t decode_noalloc_scratch(void **ptr);
+
 // Backward: workspace bytes, launch (the saving forward and the gradient kernels).
 size_t backward_workspace_bytes(int B, int T, int n_kv);
 hipError_t launch_backward(const void *qs, const void *qn, const void *k, const void *v, const void *lam,

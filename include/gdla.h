@@ -23,7 +23,8 @@
  *     (last dimension fastest) of bf16 values, unless stated otherwise, and
  *     must be 16-byte aligned.  The caller owns all memory; the library
  *     allocates nothing, keeps no pointer after the call returns, and holds no
- *     mutable global state besides a per-thread error-detail string.
+ *     mutable global state besides a per-thread error-detail string (and the
+ *     per-GPU scratch array of gdla_decode_noalloc, described there).
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *     Work is enqueued on it and the call returns without waiting; the caller
  *     synchronises before reading `out`.
@@ -164,6 +165,32 @@ int gdla_decode(const void *q_signal, const void *q_noise, const void *k_cache,
                 void *workspace, size_t workspace_bytes,
                 int B, int n_kv, int group, int d_qk, int d_v,
                 int window, float softmax_scale, void *stream);
+
+/*
+ * gdla_decode_noalloc -- gdla_decode for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same arguments without the workspace, the same
+ * kernels and the same result, bit for bit.  The split partials go to a
+ * scratch array inside the library instead: one per GPU, of
+ * gdla_decode_noalloc_max_scratch() bytes (96 MiB), held from the library's
+ * first use on that GPU until the process ends.  The call itself allocates
+ * nothing (no hipMalloc, hipFree or allocating library routine); its first
+ * call on a GPU looks up that GPU's scratch address.
+ *
+ * A call whose partials would need more than that
+ * (gdla_decode_workspace_size(B, n_kv, max_seqlen_k, window) bytes) returns
+ * GDLA_ERR_WORKSPACE and launches nothing; 64 sequences of up to 65,536
+ * cached tokens over 16 KV heads need 82 MiB.  Every call on one GPU shares
+ * its scratch and the scratch keeps the last call's contents: calls that
+ * overlap on one GPU (unordered streams) race, so order them on one stream.
+ * Arguments, limits and errors otherwise as for gdla_decode.
+ */
+size_t gdla_decode_noalloc_max_scratch(void);
+int gdla_decode_noalloc(const void *q_signal, const void *q_noise, const void *k_cache,
+                        const void *v_cache, const int32_t *cu_seqlens_k, int max_seqlen_k,
+                        const void *lambda_, const void *gate, void *out,
+                        int B, int n_kv, int group, int d_qk, int d_v,
+                        int window, float softmax_scale, void *stream);
 
 /*
  * gdla_decode_latent_workspace_size -- bytes of device workspace

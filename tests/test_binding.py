@@ -28,6 +28,8 @@ def _calls():
                                                      out=z(B, 1, s, 128)),
         "decode": lambda: api.decode(z(2, s, 192), z(2, kv, 192), z(5, kv, 192), z(5, kv, 128), i32, 3, z(2, s),
                                      z(2, s, 128), out=z(2, s, 128), workspace=torch.zeros(16, dtype=torch.uint8)),
+        "decode_noalloc": lambda: api.decode_noalloc(z(2, s, 192), z(2, kv, 192), z(5, kv, 192), z(5, kv, 128),
+                                                     i32, 3, z(2, s), z(2, s, 128), out=z(2, s, 128)),
         "decode_latent": lambda: api.decode_latent(z(2, s, 192), z(2, kv, 192), z(5, 576), i32, 3,
                                                    z(kv, 128, 512), z(kv, 128, 512), z(2, s), z(2, s, 128),
                                                    out=z(2, s, 128), workspace=torch.zeros(256, dtype=torch.uint8)),
@@ -67,6 +69,6 @@ def test_no_wait_without_sync_check(stubbed, monkeypatch, value):
 def test_every_entry_point_is_covered():
     public = {n for n in gdla.__all__} if hasattr(gdla, "__all__") else {
         n for n in dir(api) if not n.startswith("_") and callable(getattr(api, n))}
-    launchers = {n for n in public if n in ("prefill", "prefill_prefix", "decode", "decode_latent",
+    launchers = {n for n in public if n in ("prefill", "prefill_prefix", "decode", "decode_noalloc", "decode_latent",
                                             "prep", "prefill_backward")}
     assert launchers == set(_calls())

@@ -155,6 +155,40 @@ def test_decode_rejects_overlapping_workspace(lib):
     assert lib.gdla_decode_workspace_size(2, 16, 65536, 128) == 0
 
 
+def decode_noalloc(lib, ptrs=None, cu=A + 0x700000000, max_len=4096, B=2, n_kv=16, group=4, d_qk=192,
+                   d_v=128, window=0, scale=0.07):
+    if ptrs is None:
+        ptrs = [A + i * (1 << 32) for i in range(7)]
+    qs, qn, kc, vc, lam, gate, out = ptrs
+    return lib.gdla_decode_noalloc(qs, qn, kc, vc, cu, max_len, lam, gate, out, B, n_kv, group, d_qk, d_v,
+                                   window, ctypes.c_float(scale), None)
+
+
+def test_decode_noalloc_rejections(lib):
+    """Checked on the host before any HIP call, like gdla_decode; a request
+    beyond the library's scratch is GDLA_ERR_WORKSPACE."""
+    cap = lib.gdla_decode_noalloc_max_scratch()
+    assert cap == 96 << 20
+    assert lib.gdla_decode_workspace_size(64, 16, 65536, 0) <= cap          # the 64-sequence decode fits
+    assert decode_noalloc(lib, B=-1) == INVALID
+    assert decode_noalloc(lib, group=2) == UNSUPPORTED
+    assert decode_noalloc(lib, max_len=0) == INVALID
+    assert decode_noalloc(lib, cu=None) == INVALID
+    for i in range(7):
+        ptrs = [A + k * (1 << 32) for k in range(7)]
+        ptrs[i] = None
+        assert decode_noalloc(lib, ptrs) == INVALID
+        ptrs[i] = A + 4 + i * (1 << 32)
+        assert decode_noalloc(lib, ptrs) == MISALIGNED
+    assert lib.gdla_decode_workspace_size(64, 16, 1 << 30, 0) > cap
+    assert decode_noalloc(lib, B=64, max_len=1 << 30) == WORKSPACE
+    assert b"scratch" in lib.gdla_last_error()
+    ptrs = [A + k * (1 << 32) for k in range(7)]
+    ptrs[6] = ptrs[5] + 64
+    assert decode_noalloc(lib, ptrs) == INVALID
+    assert decode_noalloc(lib, [None] * 7, cu=None, B=0) == OK
+
+
 def test_decode_empty_is_noop(lib):
     assert decode(lib, [None] * 7, cu=None, B=0) == OK
 
