@@ -9,6 +9,7 @@
 
 namespace gdla {
 
+
 // Prefill of Tq query rows per sequence at positions P .. P+Tq-1 over P+Tq key rows.
 // save_hs / save_hn / save_lse non-null (with P = 0): also write the per-head
 // outputs and the log2-sum-exp of every head's softmax row
