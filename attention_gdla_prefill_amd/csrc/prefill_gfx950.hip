@@ -346,10 +346,16 @@ __device__ __forceinline__ void run(const PrefillParams &p, KRing &kring, VRing 
 #pragma unroll
             for (int kk = 0; kk < KK; ++kk) kf[kk] = *reinterpret_cast<const bf16x8 *>(kr + 32 * kk);
             f32x4 s[NH];
+            // While a wave issues a chain of matrix products it outranks the
+            // other wave of its SIMD, whose softmax arithmetic then fills the
+            // issue slots between them; when both waves reach their products
+            // together one runs ahead, which moves the pair out of step.
+            if constexpr (!TRAIN) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
             for (int kk = 0; kk < KK; ++kk)
 #pragma unroll
                 for (int h = 0; h < NH; ++h) s[h] = mfma16(kf[kk], qf[h][kk], kk == 0 ? bias[kb] : s[h]);
+            if constexpr (!TRAIN) __builtin_amdgcn_s_setprio(0);
 #pragma unroll
             for (int h = 0; h < NH; ++h) {
                 float pv[4];
@@ -370,6 +376,7 @@ __device__ __forceinline__ void run(const PrefillParams &p, KRing &kring, VRing 
         // O^T += V^T P^T: lane (r, g) receives V[4g + e][col] and V[16 + 4g + e][col],
         // col = 32c + 8(r/4) + 4s + r%4 of block 2c + s
         const __bf16 *vrd = vs + (32 * s32 + 4 * g + (r >> 2)) * VS_ROW + 8 * (r & 3);
+        if constexpr (!TRAIN) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int cb = 0; cb < D_V / 16; ++cb) {
             const int cc = 32 * (cb >> 1) + 4 * (cb & 1);
@@ -378,6 +385,7 @@ __device__ __forceinline__ void run(const PrefillParams &p, KRing &kring, VRing 
 #pragma unroll
             for (int h = 0; h < NH; ++h) o[h][cb] = mfma16(va, pb[h], o[h][cb]);
         }
+        if constexpr (!TRAIN) __builtin_amdgcn_s_setprio(0);
     };
 
     auto max_slice = [&](int s32, const __bf16 *ks, const f32x4 (&bias)[2]) {
