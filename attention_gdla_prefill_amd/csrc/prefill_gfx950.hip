@@ -309,13 +309,23 @@ __device__ __forceinline__ void run(const PrefillParams &p, KRing &kring, VRing 
     };
 
     // the reference of each row: the largest score over the visible keys of
-    // the row's own 16-key block (K rows tw .. tw+15 from global memory)
-    auto ref_pass = [&]() {
-        const int ln = lane_now();
-        const uint32_t koff = (uint32_t)(tw + (ln & 15)) * krow_b + 16 * (ln >> 4);
+    // the row's own 16-key block, K rows tw .. tw+15 -- rows 16*sub .. of the
+    // diagonal key tile kt_diag.  Every copy issued so far has landed and is
+    // visible when a query tile starts, so while that tile is still in the
+    // ring (a sliding window, the first query tiles) its rows come from LDS,
+    // else from global memory.
+    auto ref_pass = [&](int kt_diag) {
         bf16x8 kf[KK];
+        if (kt_diag >= next_copy - 3 && kt_diag < next_copy) {
+            const __bf16 *kr = kring[kt_diag % 3] + (tw - kt_diag * BN + r) * KS_ROW + 8 * g;
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) kf[kk] = __builtin_bit_cast(bf16x8, bld16(k_rsrc, koff + 64 * kk));
+            for (int kk = 0; kk < KK; ++kk) kf[kk] = *reinterpret_cast<const bf16x8 *>(kr + 32 * kk);
+        } else {
+            const int ln = lane_now();
+            const uint32_t koff = (uint32_t)(tw + (ln & 15)) * krow_b + 16 * (ln >> 4);
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk) kf[kk] = __builtin_bit_cast(bf16x8, bld16(k_rsrc, koff + 64 * kk));
+        }
         f32x4 bias[2];
         make_bias(tw, bias);
         f32x4 sd[NH];
@@ -457,7 +467,7 @@ __device__ __forceinline__ void run(const PrefillParams &p, KRing &kring, VRing 
 #pragma unroll
             for (int cb = 0; cb < D_V / 16; ++cb) o[h][cb] = zero4;
         }
-        ref_pass();
+        ref_pass(kt_hi);
         if (run_tiles(qt, kt_lo, kt_hi, next_lo, 0)) {
             wait_vmem();
             __syncthreads();
@@ -519,7 +529,11 @@ __device__ __forceinline__ void run(const PrefillParams &p, KRing &kring, VRing 
         const uint32_t lw = __builtin_amdgcn_raw_buffer_load_b32(
             l_rs, (uint32_t)edt * (uint32_t)(n_sig * 2) + 2 * R::out_head(0), 0, 0);
         load_q(n_qt, (long)n_b * Tq, n_j);
-        uint32_t so = e_off;
+        // output stores cover whole 128-byte lines: store k of a half writes
+        // rows 8k .. 8k+7, eight 16-byte chunks each; lanes r and r ^ 8 swap the
+        // chunk the other one stores (see below)
+        const int ehalf = (eln & 15) >> 3;
+        uint32_t so = (uint32_t)(tw + (eln & 7) - e_lo) * (uint32_t)(n_sig * D_V * 2) + 16 * (eln >> 4) + 64 * ehalf;
         asm volatile("" : "+v"(so));
 
         float inv[NH];
@@ -542,6 +556,14 @@ __device__ __forceinline__ void run(const PrefillParams &p, KRing &kring, VRing 
                     *reinterpret_cast<f32x4 *>(xch + 8 * cc + 4) = f32x4{hn[cc][4], hn[cc][5], hn[cc][6], hn[cc][7]};
                 }
             }
+            if (half == 0) {
+                // every K/V copy issued before this epilogue has landed (they
+                // are older than its gate, lambda and query loads), so after the
+                // barrier below the next query tile may read any tile in the ring
+                constexpr int vm = D_V / 32 * R::NOUT + 1 + NH * KK;
+                static_assert(vm < 64, "vmcnt range");
+                __builtin_amdgcn_s_waitcnt((vm & 15) | ((vm >> 4) << 14) | 0x0F70);
+            }
             lds_barrier();         // the half of H_N is in LDS
             if constexpr (ROLE == 1) {
 #pragma unroll
@@ -555,13 +577,14 @@ __device__ __forceinline__ void run(const PrefillParams &p, KRing &kring, VRing 
                     }
                 }
             }
+            u32x4 yw[R::NOUT][2];
 #pragma unroll
             for (int cc = 0; cc < 2; ++cc) {
                 const int c = 2 * half + cc;
                 const int col = 32 * c + 8 * g;
 #pragma unroll
                 for (int i = 0; i < R::NOUT; ++i) {
-                    const int h = ROLE == 0 ? i : i;   // local index of the output head
+                    const int h = i;   // local index of the output head
                     float y[8], hs[8];
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
@@ -570,9 +593,8 @@ __device__ __forceinline__ void run(const PrefillParams &p, KRing &kring, VRing 
                         hs[e] = o[h][2 * c + e / 4][e % 4] * inv[h];
                         y[e] = gv * fmaf(-lam[i], hn[cc][e], hs[e]);
                     }
-                    bst16(o_rs, so + R::out_head(i) * D_V * 2 + 64 * c,
-                          u32x4{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]), pack_bf16x2(y[4], y[5]),
-                                pack_bf16x2(y[6], y[7])});
+                    yw[i][cc] = u32x4{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]), pack_bf16x2(y[4], y[5]),
+                                      pack_bf16x2(y[6], y[7])};
                     if constexpr (TRAIN) if (row_ok)
                         *reinterpret_cast<u32x4 *>(p.hs + (row * n_sig + GROUP * j + R::out_head(i)) * D_V + col) =
                             u32x4{pack_bf16x2(hs[0], hs[1]), pack_bf16x2(hs[2], hs[3]), pack_bf16x2(hs[4], hs[5]),
@@ -582,6 +604,26 @@ __device__ __forceinline__ void run(const PrefillParams &p, KRing &kring, VRing 
                     *reinterpret_cast<u32x4 *>(p.hn + (row * n_kv + j) * D_V + col) =
                         u32x4{pack_bf16x2(hn[cc][0], hn[cc][1]), pack_bf16x2(hn[cc][2], hn[cc][3]),
                               pack_bf16x2(hn[cc][4], hn[cc][5]), pack_bf16x2(hn[cc][6], hn[cc][7])};
+            }
+            // Lane r (< 8) holds chunks c0 = 2*half and c0 + 1 of row r, lane r + 8
+            // those of row r + 8: the first store writes rows 0..7 (lane r: its
+            // c0 chunk, lane r + 8: lane r's c0 + 1 chunk), the second rows 8..15
+            // (lane r: lane r + 8's c0 chunk, lane r + 8: its own c0 + 1 chunk).
+            // Each lane hands over the chunk the other one stores (16-lane row
+            // rotation by 8: lane l <-> l ^ 8).
+#pragma unroll
+            for (int i = 0; i < R::NOUT; ++i) {
+                u32x4 give, got, first, second;
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    give[w] = ehalf ? yw[i][0][w] : yw[i][1][w];
+                    got[w] = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)give[w], 0x128, 0xF, 0xF, false);
+                    first[w] = ehalf ? got[w] : yw[i][0][w];
+                    second[w] = ehalf ? yw[i][1][w] : got[w];
+                }
+                const uint32_t ho = so + R::out_head(i) * D_V * 2 + 128 * half;
+                bst16(o_rs, ho, first);
+                bst16(o_rs, ho + 8 * (uint32_t)(n_sig * D_V * 2), second);
             }
             if (half == 0) lds_barrier();   // B has read the first half before A overwrites it
         }

@@ -128,8 +128,11 @@ def test_prefill_global_offsets_inside_sequence(T, n_kv):
 
 def prefill_schedule(T, window, P=0, run_len=None):
     """Replay of the kernel's tile schedule for one work item's runs: for each
-    query tile, the tiles it reads, and at each tile end the copies issued and
-    the wait.  Yields events (kind, tile) in program order for one wave."""
+    query tile, the reference pass (which reads the diagonal tile's K rows from
+    the ring while that tile is still there), the tiles it reads, at each tile
+    end the copies issued and the wait, and the epilogue's wait for every copy
+    issued before it and its barrier.  Yields events (kind, tile) in program
+    order for one wave."""
     BM = 64
     q0 = P // BM * BM
     Tk = T
@@ -151,6 +154,8 @@ def prefill_schedule(T, window, P=0, run_len=None):
         for qt in range(first, end):
             lo, hi = tile_lo(qt), tile_hi(qt)
             next_lo = tile_lo(qt + 1) if qt + 1 < end else 1 << 30
+            if nxt - 3 <= hi < nxt:
+                events.append(("read", hi))                 # reference pass from LDS
             for kt in range(lo, hi + 1):
                 events.append(("read", kt))
                 last = kt == hi
@@ -160,7 +165,20 @@ def prefill_schedule(T, window, P=0, run_len=None):
                     events.append(("copy", nxt)); nxt += 1
                 events.append(("wait_but_newest", nxt - 1) if nxt - 1 > nt else ("wait_all", None))
                 events.append(("barrier", None))
+            events.append(("wait_all", None))               # epilogue: copies older than its loads
+            events.append(("barrier", None))
         yield events
+
+
+def test_prefill_reference_pass_reads_ring_in_window_runs():
+    """In a run of query tiles of a 128-token window every reference pass
+    after the first finds the diagonal tile in the ring."""
+    for events in prefill_schedule(4096, 128, 0):
+        reads = [t for kind, t in events if kind == "read"]
+        n_qt = 4096 // 64
+        # three key tiles per query tile (two for the first two) plus one
+        # reference read per query tile
+        assert len(reads) == sum(min(qt, 2) + 1 for qt in range(n_qt)) + n_qt
 
 
 def check_schedule(events):
