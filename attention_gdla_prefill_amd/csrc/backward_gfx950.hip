@@ -17,10 +17,15 @@
 //
 // Kernels (all deterministic: every output element is summed by one lane):
 //   bwd_pre_kernel   the element-wise differential/gate part, dH and delta;
-//   bwd_dkdv_kernel  per (sequence, KV head, 64-key block): wave w owns 16 keys
-//                    and walks every query tile that sees them for all 5 heads;
-//   bwd_dq_kernel    per (sequence, KV head, 64-query tile): wave w owns 16
-//                    queries and walks every key block they see, head by head.
+//   bwd_dkdv_kernel  per (sequence, KV head, 128-key block): wave w of 8 owns
+//                    16 keys and walks every query tile that sees them for all
+//                    5 heads;
+//   bwd_dq_kernel    per (sequence, KV head, 128-query tile): wave w of 8 owns
+//                    16 queries and walks every key block they see, head by
+//                    head.
+// Two waves per SIMD (at most 256 registers each): while one wave waits on an
+// LDS read or its exponentials, the other's products keep the matrix core
+// busy, and every 64-row tile in LDS serves eight waves.
 // Products are bf16 MFMA (16x16x32) with fp32 accumulation; operands that
 // have to be transposed come from LDS through the transposing reads.
 #include "gdla_device.h"
@@ -29,7 +34,10 @@
 namespace gdla {
 
 constexpr int BW_T = 64;                   // query tile and key block
-constexpr int BW_THREADS = 256;
+constexpr int BW_THREADS = 256;            // element-wise kernel
+constexpr int BW_GW = 8;                   // waves of a gradient workgroup (two per SIMD)
+constexpr int BW_GRAD_THREADS = 64 * BW_GW;
+constexpr int BW_OWN = 16 * BW_GW;         // keys (dK/dV) or queries (dQ) of a gradient workgroup
 // LDS rows padded by 32 bytes: the 16 rows a fragment read or a transposing
 // read touches then fall in distinct banks (a 16-byte pad leaves ~40 % of the
 // LDS cycles in bank conflicts)
@@ -98,13 +106,13 @@ __device__ __forceinline__ uint32_t bw_lds(const T *p) {
 // pad): each copy instruction covers whole rows (2 rows of 26 chunks for the
 // 192-wide tiles, 3 rows of 18 chunks for the 128-wide ones), so a lane's row
 // and chunk within an instruction are fixed and the pad chunks are skipped;
-// wave w issues instructions w, w+4, ...
+// wave w issues instructions w, w+8, ...
 template <int COLS, int RS>
 struct BwTileCopy {
     static constexpr int CH = RS / 8;                 // 16-byte chunks per LDS row
     static constexpr int ROWS = 64 / CH;              // rows per instruction
     static constexpr int N = (BW_T + ROWS - 1) / ROWS;
-    static constexpr int PER_WAVE = (N + 3) / 4;
+    static constexpr int PER_WAVE = (N + BW_GW - 1) / BW_GW;
     int lr, ch;
     __device__ __forceinline__ void init(int lane) {
         lr = lane / CH;
@@ -114,7 +122,7 @@ struct BwTileCopy {
     __device__ __forceinline__ void issue(const bw_i32x4 &rsrc, uint32_t row_bytes, uint32_t lds_tile, int wave) const {
 #pragma unroll
         for (int c = 0; c < PER_WAVE; ++c) {
-            const int row0 = ROWS * (wave + 4 * c);
+            const int row0 = ROWS * (wave + BW_GW * c);
             if (row0 < BW_T && lr < ROWS && ch < COLS / 8 && row0 + lr < BW_T)
                 bw_copy16(rsrc, (uint32_t)(row0 + lr) * row_bytes + 16 * ch, lds_tile + (uint32_t)(row0 * RS * 2));
         }
@@ -210,19 +218,20 @@ __device__ __forceinline__ BwHead bw_head(const BwdParams &p, int b, int j, int 
     return x;
 }
 
-// ---- 2. dK, dV.  Workgroup (KV head j, 64-key block, sequence b); wave w owns
-// keys kb0 + 16w .. +15.  Steps: (query tile, head) for every query tile that
+// ---- 2. dK, dV.  Workgroup (KV head j, 128-key block, sequence b); wave w owns
+// keys kb0 + 16w .. +15 (the first query tile of the block sees none of the
+// keys of waves 4..7: their weights there are 0).  Steps: (query tile, head) for every query tile that
 // sees a key of the block and each of the 5 heads; the Q and dH tiles, the
 // log2-sum-exp and delta of a step are copied two steps ahead into a ring of
 // three LDS slots.  In C layout lane (r, g) holds element [query 16qb + 4g + e]
 // [key r] of S, P, dP, dS.
-__global__ __launch_bounds__(BW_THREADS, 1) void bwd_dkdv_kernel(BwdParams p) {
+__global__ __launch_bounds__(BW_GRAD_THREADS, 1) void bwd_dkdv_kernel(BwdParams p) {
     __shared__ __attribute__((aligned(16))) __bf16 Qs[3][BW_T * BW_QROW];
     __shared__ __attribute__((aligned(16))) __bf16 Hs[3][BW_T * BW_VROW];
     __shared__ __attribute__((aligned(16))) float lse_s[3][BW_T], dl_s[3][BW_T];
     // the KV head is the fastest grid index, so the workgroups are dispatched
     // longest first (key block 0 sees every query tile)
-    const int j = blockIdx.x, kb0 = blockIdx.y * BW_T, b = blockIdx.z;
+    const int j = blockIdx.x, kb0 = blockIdx.y * BW_OWN, b = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, r = lane & 15, g = lane >> 4;
     const int n_h = p.n_kv * HEADS, T = p.T;
     const int key = kb0 + 16 * wave + r;
@@ -248,7 +257,7 @@ __global__ __launch_bounds__(BW_THREADS, 1) void bwd_dkdv_kernel(BwdParams p) {
     // query tiles that see a key of this block
     const int qt_lo = kb0 / BW_T;
     int qt_hi = (T - 1) / BW_T;
-    if (p.window > 0) qt_hi = min(qt_hi, (kb0 + BW_T - 1 + p.window - 1) / BW_T);
+    if (p.window > 0) qt_hi = min(qt_hi, (kb0 + BW_OWN - 1 + p.window - 1) / BW_T);
     const int n_steps = (qt_hi - qt_lo + 1) * HEADS;
     BwTileCopy<D_QK, BW_QROW> cq;
     BwTileCopy<D_V, BW_VROW> ch;
@@ -275,55 +284,45 @@ __global__ __launch_bounds__(BW_THREADS, 1) void bwd_dkdv_kernel(BwdParams p) {
     for (int it = 0; it < n_steps; ++it) {
         const int buf = it % 3, q0 = (qt_lo + it / HEADS) * BW_T;
         const __bf16 *qs_ = Qs[buf], *hs_ = Hs[buf];
-        // S = Q K_w^T and dP = dH V_w^T, four 16-query blocks
-        f32x4 s[4], dp[4];
-#pragma unroll
-        for (int qb = 0; qb < 4; ++qb) {
-            const __bf16 *qa = qs_ + (16 * qb + r) * BW_QROW + 8 * g;
-            const __bf16 *ha = hs_ + (16 * qb + r) * BW_VROW + 8 * g;
-            s[qb] = zero4;
-            dp[qb] = zero4;
-#pragma unroll
-            for (int kk = 0; kk < D_QK / 32; ++kk)
-                s[qb] = mfma16(*reinterpret_cast<const bf16x8 *>(qa + 32 * kk), kf[kk], s[qb]);
-#pragma unroll
-            for (int kk = 0; kk < D_V / 32; ++kk)
-                dp[qb] = mfma16(*reinterpret_cast<const bf16x8 *>(ha + 32 * kk), vf[kk], dp[qb]);
-        }
-        // P and dS; packed as B operands over query pairs (blocks 2i, 2i+1).
-        // The rows' log2-sum-exp and delta are read first and the weight is
-        // computed for every element, then selected (no branch per element).
-        float4 lse4[4], dl4[4];
-#pragma unroll
-        for (int qb = 0; qb < 4; ++qb) {
-            lse4[qb] = *reinterpret_cast<const float4 *>(&lse_s[buf][16 * qb + 4 * g]);
-            dl4[qb] = *reinterpret_cast<const float4 *>(&dl_s[buf][16 * qb + 4 * g]);
-        }
-        uint32_t pw[4][2], sw[4][2];
-#pragma unroll
-        for (int qb = 0; qb < 4; ++qb) {
-            const float ls[4] = {lse4[qb].x, lse4[qb].y, lse4[qb].z, lse4[qb].w};
-            const float dls[4] = {dl4[qb].x, dl4[qb].y, dl4[qb].z, dl4[qb].w};
-            float pv[4], dsv[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int ql = 16 * qb + 4 * g + e;
-                const float x = fast_exp2(fmaf(s[qb][e], p.scale_log2, -ls[e]));
-                pv[e] = bw_visible(q0 + ql, key, T, p.window) ? x : 0.f;
-                dsv[e] = pv[e] * (dp[qb][e] - dls[e]);
-            }
-            pw[qb][0] = pack_bf16x2(pv[0], pv[1]);
-            pw[qb][1] = pack_bf16x2(pv[2], pv[3]);
-            sw[qb][0] = pack_bf16x2(dsv[0], dsv[1]);
-            sw[qb][1] = pack_bf16x2(dsv[2], dsv[3]);
-        }
+        // Two halves of 32 queries (16-query blocks 2i, 2i+1): S = Q K_w^T and
+        // dP = dH V_w^T, then P and dS packed as B operands over the pair, then
+        // dV^T += dH^T P and dK^T += Q^T dS.  The rows' log2-sum-exp and delta
+        // are read first and the weight is computed for every element, then
+        // selected (no branch per element).
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-            const bf16x8 pb = __builtin_bit_cast(bf16x8, (u32x4{pw[2 * i][0], pw[2 * i][1], pw[2 * i + 1][0],
-                                                                pw[2 * i + 1][1]}));
-            const bf16x8 sb = __builtin_bit_cast(bf16x8, (u32x4{sw[2 * i][0], sw[2 * i][1], sw[2 * i + 1][0],
-                                                                sw[2 * i + 1][1]}));
-            // dV^T += dH^T P, dK^T += Q^T dS over the 32 queries of pair i
+            uint32_t pw[2][2], sw[2][2];
+#pragma unroll
+            for (int hb = 0; hb < 2; ++hb) {
+                const int qb = 2 * i + hb;
+                const __bf16 *qa = qs_ + (16 * qb + r) * BW_QROW + 8 * g;
+                const __bf16 *ha = hs_ + (16 * qb + r) * BW_VROW + 8 * g;
+                f32x4 sv = zero4, dpv = zero4;
+#pragma unroll
+                for (int kk = 0; kk < D_QK / 32; ++kk)
+                    sv = mfma16(*reinterpret_cast<const bf16x8 *>(qa + 32 * kk), kf[kk], sv);
+#pragma unroll
+                for (int kk = 0; kk < D_V / 32; ++kk)
+                    dpv = mfma16(*reinterpret_cast<const bf16x8 *>(ha + 32 * kk), vf[kk], dpv);
+                const float4 lse4 = *reinterpret_cast<const float4 *>(&lse_s[buf][16 * qb + 4 * g]);
+                const float4 dl4 = *reinterpret_cast<const float4 *>(&dl_s[buf][16 * qb + 4 * g]);
+                const float ls[4] = {lse4.x, lse4.y, lse4.z, lse4.w};
+                const float dls[4] = {dl4.x, dl4.y, dl4.z, dl4.w};
+                float pv[4], dsv[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int ql = 16 * qb + 4 * g + e;
+                    const float x = fast_exp2(fmaf(sv[e], p.scale_log2, -ls[e]));
+                    pv[e] = bw_visible(q0 + ql, key, T, p.window) ? x : 0.f;
+                    dsv[e] = pv[e] * (dpv[e] - dls[e]);
+                }
+                pw[hb][0] = pack_bf16x2(pv[0], pv[1]);
+                pw[hb][1] = pack_bf16x2(pv[2], pv[3]);
+                sw[hb][0] = pack_bf16x2(dsv[0], dsv[1]);
+                sw[hb][1] = pack_bf16x2(dsv[2], dsv[3]);
+            }
+            const bf16x8 pb = __builtin_bit_cast(bf16x8, (u32x4{pw[0][0], pw[0][1], pw[1][0], pw[1][1]}));
+            const bf16x8 sb = __builtin_bit_cast(bf16x8, (u32x4{sw[0][0], sw[0][1], sw[1][0], sw[1][1]}));
 #pragma unroll
             for (int db = 0; db < D_V / 16; ++db) dv[db] = mfma16(bw_tr_a(hs_, BW_VROW, 32 * i, 16 * db, r, g), pb, dv[db]);
 #pragma unroll
@@ -331,10 +330,11 @@ __global__ __launch_bounds__(BW_THREADS, 1) void bwd_dkdv_kernel(BwdParams p) {
         }
         // step it+2 into the slot of step it-1, which every wave finished
         // before the previous barrier; then step it+1 must have landed (only
-        // the copies just issued may stay in flight) before the bare barrier
+        // the copies just issued -- 6 to 8 per wave -- may stay in flight)
+        // before the bare barrier
         if (it + 2 < n_steps) {
             issue(it + 2);
-            __builtin_amdgcn_s_waitcnt(0x007D);   // vmcnt(13) lgkmcnt(0)
+            __builtin_amdgcn_s_waitcnt(0x0076);   // vmcnt(6) lgkmcnt(0)
         } else {
             __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
         }
@@ -356,23 +356,24 @@ __global__ __launch_bounds__(BW_THREADS, 1) void bwd_dkdv_kernel(BwdParams p) {
     }
 }
 
-// ---- 3. dQ.  Workgroup (KV head j, 64-query tile, sequence b); wave w owns
-// queries q0 + 16w .. +15.  Steps: (head, key block) over the 5 heads and the
+// ---- 3. dQ.  Workgroup (KV head j, 128-query tile, sequence b); wave w owns
+// queries q0 + 16w .. +15 (the last key block of the tile is hidden from the
+// queries of waves 0..3: their weights there are 0).  Steps: (head, key block) over the 5 heads and the
 // key blocks the tile sees; the K and V tiles of a step are copied two steps
 // ahead into a ring of three LDS slots.  In C layout lane (r, g) holds element
 // [key 16kb + 4g + e][query r] of S^T, P^T, dP^T, dS^T.
-__global__ __launch_bounds__(BW_THREADS, 1) void bwd_dq_kernel(BwdParams p) {
+__global__ __launch_bounds__(BW_GRAD_THREADS, 1) void bwd_dq_kernel(BwdParams p) {
     __shared__ __attribute__((aligned(16))) __bf16 Ks[3][BW_T * BW_QROW];
     __shared__ __attribute__((aligned(16))) __bf16 Vs[3][BW_T * BW_VROW];
     // longest first: the last query tiles see the most key blocks
-    const int j = blockIdx.x, q0 = (gridDim.y - 1 - blockIdx.y) * BW_T, b = blockIdx.z;
+    const int j = blockIdx.x, q0 = (gridDim.y - 1 - blockIdx.y) * BW_OWN, b = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, r = lane & 15, g = lane >> 4;
     const int n_h = p.n_kv * HEADS, T = p.T;
     const int q = q0 + 16 * wave + r;
     const bool q_ok = q < T;
     const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
     const int kb_lo = p.window > 0 ? max(0, q0 - p.window + 1) / BW_T : 0;
-    const int kb_hi = (min(q0 + BW_T, T) - 1) / BW_T;
+    const int kb_hi = (min(q0 + BW_OWN, T) - 1) / BW_T;
     const int n_kb = kb_hi - kb_lo + 1, n_steps = HEADS * n_kb;
     const __bf16 *kseq = p.k + ((long)b * T * p.n_kv + j) * D_QK;
     const __bf16 *vseq = p.v + ((long)b * T * p.n_kv + j) * D_V;
@@ -461,9 +462,10 @@ __global__ __launch_bounds__(BW_THREADS, 1) void bwd_dq_kernel(BwdParams p) {
         }
         // step it+2 into the slot of step it-1 (finished by every wave before
         // the previous barrier); step it+1 must have landed before the barrier
+        // (the 6 or 7 copies just issued may stay in flight)
         if (it + 2 < n_steps) {
             issue(it + 2);
-            __builtin_amdgcn_s_waitcnt(0x007D);   // vmcnt(13) lgkmcnt(0)
+            __builtin_amdgcn_s_waitcnt(0x0076);   // vmcnt(6) lgkmcnt(0)
         } else {
             __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
         }
@@ -533,10 +535,10 @@ hipError_t launch_backward(const void *qs, const void *qn, const void *k, const 
     const long units = (long)B * T * n_kv;
     hipLaunchKernelGGL(bwd_pre_kernel, dim3((unsigned)((units + 7) / 8)), dim3(BW_THREADS), 0, stream, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    const unsigned n_t = (unsigned)((T + BW_T - 1) / BW_T);
-    hipLaunchKernelGGL(bwd_dkdv_kernel, dim3(n_kv, n_t, B), dim3(BW_THREADS), 0, stream, p);
+    const unsigned n_t = (unsigned)((T + BW_OWN - 1) / BW_OWN);
+    hipLaunchKernelGGL(bwd_dkdv_kernel, dim3(n_kv, n_t, B), dim3(BW_GRAD_THREADS), 0, stream, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(bwd_dq_kernel, dim3(n_kv, n_t, B), dim3(BW_THREADS), 0, stream, p);
+    hipLaunchKernelGGL(bwd_dq_kernel, dim3(n_kv, n_t, B), dim3(BW_GRAD_THREADS), 0, stream, p);
     return hipGetLastError();
 }
 
