@@ -564,6 +564,249 @@ __global__ __launch_bounds__(LT_C) void latent_combine_kernel(LatentParams p) {
     p.out[orow * D_V + d] = (__bf16)((float)p.gate[orow * D_V + d] * D);
 }
 
+// ---- window decode over the latent cache (1 <= W <= 128): the whole job of
+// one (KV head j, sequence b) in one workgroup, one launch -----------------
+//
+// With at most 128 visible rows a (sequence, KV head) is a short chain of
+// small steps, so the four launches of the split path (each of them at least
+// one HBM latency) become four phases of one workgroup, each of which issues
+// all of its loads before it waits for any (one memory round trip per phase):
+//   1. q~ = [W_uk[j]^T q^C ; q^R] of the 5 heads: thread t takes columns
+//      8(t%64) .. +7 of W_uk[j] over rows 32(t/64) .. +31 (a wave reads whole
+//      1 KB rows), the four row quarters add up through LDS; rounded to bf16
+//      into LDS as the B operand of the scores;
+//   2. S^T = L q~^T on the matrix cores, wave w taking rows 32w .. 32w+31 of
+//      the window straight from HBM as A fragments; the exact row maxima and
+//      sums meet in LDS (no fixed reference, nothing to redo), the weights go
+//      to LDS in fp32;
+//   3. o~[h][c] = sum_s p_s c_s[c] on the VALU: thread t takes columns
+//      8(t%64) .. +7 over rows 32(t/64) .. +31 of the window, the quarters
+//      add up through LDS; then the differential combine in the latent
+//      space, d~ = o~_S / l_S - lambda o~_N / l_N;
+//   4. D = W_uv[j] d~ (thread t: half of the latent values of output column
+//      t % 128), out = gate * D.
+// The row sums are taken over the fp32 weights that enter o~.
+constexpr int LW_KEYS = 128;
+constexpr int LW_THREADS = 256;
+constexpr int LW_QROW = LT_ROW + 8;           // bf16 per absorbed-query row in LDS (16-byte pad)
+static_assert(LW_THREADS * 2 == LT_C && LW_THREADS / 64 * 32 == LT_KC && LW_THREADS / 64 * 32 == LW_KEYS,
+              "thread / column / row split");
+
+__global__ __launch_bounds__(LW_THREADS, 2) void latent_window_kernel(LatentParams p) {
+    __shared__ float qc[HEADS][LT_KC];                                   // content parts of the queries
+    __shared__ __attribute__((aligned(16))) __bf16 qt_s[HEADS][LW_QROW]; // absorbed queries
+    __shared__ float red_m[4][16], red_l[4][16];
+    __shared__ __attribute__((aligned(16))) float pw_s[HEADS][LW_KEYS];  // weights
+    __shared__ __attribute__((aligned(16))) float part[4][HEADS][LT_C];  // per-quarter partial sums
+    __shared__ float dl[GROUP][LT_C];                                    // d~ of the signal heads
+
+    const int j = blockIdx.x, b = blockIdx.y;
+    const int n_kv = p.n_kv, n_sig = n_kv * GROUP;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int r = lane & 15, g = lane >> 4;
+    const int uwave = __builtin_amdgcn_readfirstlane(wave);
+
+    // ---- loads that need no offsets: cu[b], cu[b+1], W_uk[j], the queries,
+    // lambda and the gate
+    const auto cu_rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<int32_t *>(p.cu), 0, (int)((gridDim.y + 1) * 4u),
+                                                         0x00020000);
+    const u32x2 cuv = __builtin_amdgcn_raw_buffer_load_b64(cu_rs, 4u * b, 0, 0);
+    u32x4 wk[32];
+    {
+        const __bf16 *w = p.wuk + ((long)j * LT_KC + 32 * uwave) * LT_C + 8 * lane;
+#pragma unroll
+        for (int i = 0; i < 32; ++i) wk[i] = ldg16(w + i * LT_C);
+    }
+    auto q_src = [&](int h) {
+        return h < GROUP ? p.qs + ((long)b * n_sig + GROUP * j + h) * D_QK : p.qn + ((long)b * n_kv + j) * D_QK;
+    };
+    for (int i = tid; i < HEADS * D_QK; i += LW_THREADS) {
+        const int h = i / D_QK, d = i % D_QK;
+        const __bf16 v = q_src(h)[d];
+        if (d < LT_KC) qc[h][d] = (float)v;
+        else qt_s[h][LT_C + d - LT_KC] = v;            // the rotary part is used as it is
+    }
+    const long orow0 = (long)b * n_sig + GROUP * j;     // signal head 4j
+    const u32x2 lw = *reinterpret_cast<const u32x2 *>(p.lam + orow0);     // lambda of the 4 signal heads
+    const int oh = tid >> 6, oc = 2 * (tid & 63);       // output: head 4j + oh, columns oc, oc + 1
+    const uint32_t gw = *reinterpret_cast<const uint32_t *>(p.gate + (orow0 + oh) * D_V + oc);
+
+    const int start = __builtin_amdgcn_readfirstlane((int)cuv[0]);
+    const int L = __builtin_amdgcn_readfirstlane((int)cuv[1]) - start;
+    const int n_vis = max(0, min(L, p.window));         // <= LW_KEYS
+    const long row0 = (long)start + (L - n_vis);        // first visible cache row
+    const auto lat_rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<__bf16 *>(p.lat + row0 * LT_ROW), 0,
+                                                          (int)((uint32_t)n_vis * LT_ROW * 2), 0x00020000);
+    __syncthreads();
+
+    // ---- 1. absorbed queries
+    {
+        float acc[HEADS][8];
+#pragma unroll
+        for (int h = 0; h < HEADS; ++h)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+#pragma unroll
+            for (int h = 0; h < HEADS; ++h) {
+                const float q = qc[h][32 * uwave + i];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    acc[h][2 * e] = fmaf(q, bf16_lo(wk[i][e]), acc[h][2 * e]);
+                    acc[h][2 * e + 1] = fmaf(q, bf16_hi(wk[i][e]), acc[h][2 * e + 1]);
+                }
+            }
+        }
+#pragma unroll
+        for (int h = 0; h < HEADS; ++h) {
+            *reinterpret_cast<f32x4 *>(&part[wave][h][8 * lane]) = f32x4{acc[h][0], acc[h][1], acc[h][2], acc[h][3]};
+            *reinterpret_cast<f32x4 *>(&part[wave][h][8 * lane + 4]) = f32x4{acc[h][4], acc[h][5], acc[h][6], acc[h][7]};
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int h = 0; h < HEADS; ++h) {
+        float v[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+            v[i] = part[0][h][2 * tid + i] + part[1][h][2 * tid + i] + part[2][h][2 * tid + i] + part[3][h][2 * tid + i];
+        *reinterpret_cast<uint32_t *>(&qt_s[h][2 * tid]) = pack_bf16x2(v[0], v[1]);
+    }
+    __syncthreads();
+
+    // ---- 2. scores of rows 32w + 16kb + r: S^T = L q~^T (columns r >= 5 unused)
+    const float c_log2 = p.scale_log2;
+    f32x4 s[2];
+    {
+        bf16x8 la[2][LT_KK];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int k = 0; k < LT_KK; ++k)
+                la[kb][k] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                    lat_rs, (uint32_t)(32 * uwave + 16 * kb + r) * (LT_ROW * 2) + 64 * k + 16 * g, 0, 0));
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) s[kb][e] = 32 * uwave + 16 * kb + 4 * g + e < n_vis ? 0.f : -INFINITY;
+        const __bf16 *qrow = qt_s[r < HEADS ? r : 0] + 8 * g;
+        const bool q_on = r < HEADS;
+        const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int k = 0; k < LT_KK; ++k) {
+            const u32x4 qw = *reinterpret_cast<const u32x4 *>(qrow + 32 * k);
+            const bf16x8 qb = __builtin_bit_cast(bf16x8, q_on ? qw : z);
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) s[kb] = mfma16(la[kb][k], qb, s[kb]);
+        }
+    }
+    {
+        const float mx = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                               fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+        const float wm = group4_max(mx);
+        if (g == 0) red_m[wave][r] = wm;
+    }
+    __syncthreads();
+    {
+        const float m = fmaxf(fmaxf(red_m[0][r], red_m[1][r]), fmaxf(red_m[2][r], red_m[3][r]));
+        const float m_ref = m == -INFINITY ? 0.f : m * c_log2;
+        float l_part = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            f32x4 pv;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                pv[e] = fast_exp2(fmaf(s[kb][e], c_log2, -m_ref));
+                l_part += pv[e];
+            }
+            if (r < HEADS) *reinterpret_cast<f32x4 *>(&pw_s[r][32 * uwave + 16 * kb + 4 * g]) = pv;
+        }
+        const float wl = group4_sum(l_part);
+        if (g == 0) red_l[wave][r] = wl;
+    }
+    __syncthreads();
+
+    // ---- 3. o~[h][c] = sum_s p_s[h] c_s[c]: columns 8 lane .. +7 over the
+    // window rows 32w .. 32w+31 (rows past the window read zeros, weight 0)
+    {
+        u32x4 cv[32];
+#pragma unroll
+        for (int i = 0; i < 32; ++i)
+            cv[i] = __builtin_amdgcn_raw_buffer_load_b128(lat_rs, (uint32_t)(32 * uwave + i) * (LT_ROW * 2) + 16 * lane,
+                                                          0, 0);
+        float acc[HEADS][8];
+#pragma unroll
+        for (int h = 0; h < HEADS; ++h)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+#pragma unroll
+            for (int h = 0; h < HEADS; ++h) {
+                const float w = pw_s[h][32 * uwave + i];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    acc[h][2 * e] = fmaf(w, bf16_lo(cv[i][e]), acc[h][2 * e]);
+                    acc[h][2 * e + 1] = fmaf(w, bf16_hi(cv[i][e]), acc[h][2 * e + 1]);
+                }
+            }
+        }
+#pragma unroll
+        for (int h = 0; h < HEADS; ++h) {
+            *reinterpret_cast<f32x4 *>(&part[wave][h][8 * lane]) = f32x4{acc[h][0], acc[h][1], acc[h][2], acc[h][3]};
+            *reinterpret_cast<f32x4 *>(&part[wave][h][8 * lane + 4]) = f32x4{acc[h][4], acc[h][5], acc[h][6], acc[h][7]};
+        }
+    }
+    __syncthreads();
+    {
+        float inv[HEADS];
+#pragma unroll
+        for (int h = 0; h < HEADS; ++h) {
+            const float l = red_l[0][h] + red_l[1][h] + red_l[2][h] + red_l[3][h];
+            inv[h] = l > 0.f ? 1.f / l : 0.f;
+        }
+        float o[HEADS][2];
+#pragma unroll
+        for (int h = 0; h < HEADS; ++h)
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+                o[h][i] = (part[0][h][2 * tid + i] + part[1][h][2 * tid + i] + part[2][h][2 * tid + i] +
+                           part[3][h][2 * tid + i]) * inv[h];
+        const float lam[GROUP] = {bf16_lo(lw[0]), bf16_hi(lw[0]), bf16_lo(lw[1]), bf16_hi(lw[1])};
+#pragma unroll
+        for (int h = 0; h < GROUP; ++h)
+#pragma unroll
+            for (int i = 0; i < 2; ++i) dl[h][2 * tid + i] = fmaf(-lam[h], o[GROUP][i], o[h][i]);
+    }
+    __syncthreads();
+
+    // ---- 4. D[h][d] = sum_c W_uv[j][d][c] d~[h][c]: thread (half q2, column d)
+    // sums latent values 256 q2 .. +255; the halves add up through LDS
+    {
+        const int q2 = tid / D_V, d = tid % D_V, c0 = q2 * (LT_C / 2);
+        const __bf16 *w = p.wuv + ((long)j * D_V + d) * LT_C + c0;
+        u32x4 wv[LT_C / 2 / 8];
+#pragma unroll
+        for (int c = 0; c < LT_C / 2 / 8; ++c) wv[c] = ldg16(w + 8 * c);
+        float acc4[GROUP] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < LT_C / 2 / 8; ++c)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int h = 0; h < GROUP; ++h) {
+                    acc4[h] = fmaf(bf16_lo(wv[c][i]), dl[h][c0 + 8 * c + 2 * i], acc4[h]);
+                    acc4[h] = fmaf(bf16_hi(wv[c][i]), dl[h][c0 + 8 * c + 2 * i + 1], acc4[h]);
+                }
+#pragma unroll
+        for (int h = 0; h < GROUP; ++h) part[q2][h][d] = acc4[h];
+    }
+    __syncthreads();
+    const float D0 = part[0][oh][oc] + part[1][oh][oc], D1 = part[0][oh][oc + 1] + part[1][oh][oc + 1];
+    *reinterpret_cast<uint32_t *>(p.out + (orow0 + oh) * D_V + oc) = pack_bf16x2(bf16_lo(gw) * D0, bf16_hi(gw) * D1);
+}
+
 int latent_splits(int max_seqlen_k, int window) {
     const long vis = window > 0 ? (long)std::min(max_seqlen_k, window) : (long)max_seqlen_k;
     const long n = (vis + LT_CHUNK - 1) / LT_CHUNK;
@@ -618,6 +861,11 @@ hipError_t launch_decode_latent(const void *qs, const void *qn, const void *lat,
     p.n_split = n_split;
     p.window = window;
     p.scale_log2 = scale * LOG2E;
+    if (window >= 1 && window <= LW_KEYS) {
+        // a short window: one workgroup per (KV head, sequence) does it all
+        hipLaunchKernelGGL(latent_window_kernel, dim3(n_kv, B), dim3(LW_THREADS), 0, stream, p);
+        return hipGetLastError();
+    }
     hipLaunchKernelGGL(latent_absorb_kernel, dim3(n_kv, (B + LT_ABS_SEQ - 1) / LT_ABS_SEQ), dim3(LT_ABS_THREADS), 0,
                        stream, p);
     hipError_t e = hipGetLastError();

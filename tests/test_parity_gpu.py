@@ -509,6 +509,26 @@ def test_decode_latent_score_spikes():
     compare(gpu_decode_latent(d, max(lengths), 0), oracle_decode_latent(d, 0), "latent decode score spikes")
 
 
+def test_decode_latent_window_score_spikes():
+    """The one-launch window path (W <= 128) with rows whose scores stand ~180
+    log2 units above the rest: its weights are taken against the exact row
+    maxima of the window, so a spike anywhere in it (first row, last row,
+    between) must give the softmax of the oracle."""
+    n_kv, lengths = 2, [300, 5000, 70]
+    log("latent window decode score spikes lengths=%s" % lengths)
+    w, _ = latent_workload(n_kv, lengths)
+    d = W.latent_decode_inputs(w, seed=92, lengths=torch.tensor(lengths), q_std=1.0)
+    cu = d["cu_seqlens"].tolist()
+    for b, key in [(0, 300 - 128), (0, 299), (1, 4950), (2, 0), (2, 69)]:
+        row = d["latent"][cu[b] + key].float()
+        row[512:] *= 3000.0
+        d["latent"][cu[b] + key] = row.to(torch.bfloat16)
+    d = to_dev(d)
+    for window in (128, 40):
+        compare(gpu_decode_latent(d, max(lengths), window), oracle_decode_latent(d, window),
+                "latent window decode score spikes W=%d" % window)
+
+
 @pytest.mark.parametrize("name", ["dec_latent_full", "dec_latent_swa"])
 def test_decode_latent_configs_sampled(name):
     """The 64-sequence configs; sampled sequences checked against the expanded
