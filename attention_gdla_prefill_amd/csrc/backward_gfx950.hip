@@ -129,9 +129,6 @@ struct BwTileCopy {
     }
 };
 static_assert(64 / (BW_QROW / 8) == 2 && 64 / (BW_VROW / 8) == 3, "rows per copy");
-__device__ __forceinline__ bool bw_visible(int q, int key, int T, int window) {
-    return q < T && key <= q && (window == 0 || q - key < window);
-}
 
 // ---- 1. element-wise part.  32 lanes per (token, KV head j), 4 values each.
 __global__ __launch_bounds__(BW_THREADS) void bwd_pre_kernel(BwdParams p) {
@@ -288,7 +285,11 @@ __global__ __launch_bounds__(BW_GRAD_THREADS, 1) void bwd_dkdv_kernel(BwdParams 
         // dP = dH V_w^T, then P and dS packed as B operands over the pair, then
         // dV^T += dH^T P and dK^T += Q^T dS.  The rows' log2-sum-exp and delta
         // are read first and the weight is computed for every element, then
-        // selected (no branch per element).
+        // selected (no branch per element).  A pair is visible when 0 <= q -
+        // key < window (one unsigned compare); rows past the sequence end need
+        // no test: their Q, dH and delta read as zeros, so they add nothing to
+        // dV or dK whatever their weight.
+        const uint32_t wlim = p.window == 0 ? 0x7fffffffu : (uint32_t)p.window;
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             uint32_t pw[2][2], sw[2][2];
@@ -311,9 +312,8 @@ __global__ __launch_bounds__(BW_GRAD_THREADS, 1) void bwd_dkdv_kernel(BwdParams 
                 float pv[4], dsv[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const int ql = 16 * qb + 4 * g + e;
                     const float x = fast_exp2(fmaf(sv[e], p.scale_log2, -ls[e]));
-                    pv[e] = bw_visible(q0 + ql, key, T, p.window) ? x : 0.f;
+                    pv[e] = (uint32_t)(q0 + 16 * qb + 4 * g + e - key) < wlim ? x : 0.f;
                     dsv[e] = pv[e] * (dpv[e] - dls[e]);
                 }
                 pw[hb][0] = pack_bf16x2(pv[0], pv[1]);
@@ -419,6 +419,9 @@ __global__ __launch_bounds__(BW_GRAD_THREADS, 1) void bwd_dq_kernel(BwdParams p)
             for (int i = 0; i < D_QK / 16; ++i) dq[i] = zero4;
         }
         const __bf16 *ks_ = Ks[buf], *vs_ = Vs[buf];
+        // a pair is visible when 0 <= q - key < window (one unsigned compare);
+        // keys past the sequence end read zero K rows and add nothing to dQ
+        const uint32_t wlim = p.window == 0 ? 0x7fffffffu : (uint32_t)p.window;
         uint32_t sw[4][2];
 #pragma unroll
         for (int k4 = 0; k4 < 4; ++k4) {
@@ -434,9 +437,8 @@ __global__ __launch_bounds__(BW_GRAD_THREADS, 1) void bwd_dq_kernel(BwdParams p)
             float dsv[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int key = k0 + 16 * k4 + 4 * g + e;
                 const float x = fast_exp2(fmaf(stv[e], p.scale_log2, -lse));
-                const float pv = bw_visible(q, key, T, p.window) ? x : 0.f;
+                const float pv = (uint32_t)(q - (k0 + 16 * k4 + 4 * g + e)) < wlim ? x : 0.f;
                 dsv[e] = pv * (dpt[e] - dl);
             }
             sw[k4][0] = pack_bf16x2(dsv[0], dsv[1]);
