@@ -52,6 +52,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <cstdlib>
 
 namespace gdla {
 
@@ -681,6 +682,19 @@ static int compute_units() {
     return n;
 }
 
+// Test knobs, read at every launch: GDLA_PREFILL_GRID caps the number of
+// persistent workgroups, GDLA_PREFILL_RUN_LEN sets the query tiles per work
+// item of a sliding window of up to 2*BN+1 keys.  The output does not depend
+// on either (a query tile's arithmetic is the same in any schedule); the tests
+// compare schedules bit for bit.
+static long env_knob(const char *name) {
+    const char *e = std::getenv(name);
+    if (!e || !*e) return 0;
+    char *end = nullptr;
+    const long v = std::strtol(e, &end, 10);
+    return (end && *end == 0 && v > 0) ? v : 0;
+}
+
 hipError_t launch_prefill(const void *qs, const void *qn, const void *k, const void *v,
                           const void *lam, const void *gate, void *out, int B, int Tq, int P, int n_kv,
                           int window, float scale, hipStream_t stream, void *save_hs, void *save_hn,
@@ -711,11 +725,13 @@ hipError_t launch_prefill(const void *qs, const void *qn, const void *k, const v
     if (p.window > 0 && p.window <= 2 * pf::BN + 1) {
         const long tiles = (long)B * n_kv * p.n_qt;
         p.run_len = (int)std::max(1L, std::min((long)p.n_qt, (tiles + 2L * n_cu - 1) / (2L * n_cu)));
+        if (const long rl = env_knob("GDLA_PREFILL_RUN_LEN")) p.run_len = (int)std::min((long)p.n_qt, rl);
     }
     p.n_runs = (p.n_qt + p.run_len - 1) / p.run_len;
     // one persistent workgroup per CU (at most one fits: LDS and registers)
     const long items = (long)B * n_kv * p.n_runs;
-    const long blocks = std::min(items, (long)n_cu);
+    long blocks = std::min(items, (long)n_cu);
+    if (const long g = env_knob("GDLA_PREFILL_GRID")) blocks = std::min(blocks, g);
     if (save_hs)        // the saving mode (a full prefill only)
         hipLaunchKernelGGL((pf::prefill_kernel<false, true>), dim3((unsigned)blocks), dim3(pf::THREADS), 0, stream, p);
     else if (P > 0)

@@ -113,6 +113,35 @@ def test_prefill_deterministic():
     assert torch.equal(a, b)
 
 
+@pytest.mark.parametrize("window", [0, 77, 128, 129, 300])
+def test_prefill_schedule_does_not_change_results(monkeypatch, window):
+    """Alternative schedules give the same output bit for bit: fewer persistent
+    workgroups than CUs (1, 7, 8 and 24: every workgroup walks many work items,
+    with and without the per-XCD dealing) and, for windows of up to 129 keys,
+    other run lengths (1, 2, 5 query tiles per work item).  Half the keys carry
+    a steep ramp, so query tiles are also redone against their exact maxima
+    inside the runs."""
+    x = to_dev(W.prefill_inputs(small(2, 1000, 8, window), seed=21, **SHARP))
+    pos = torch.arange(1000, device="cuda")
+    x["q_signal"][1, ..., 0] = 16.0
+    x["q_noise"][1, ..., 0] = 16.0
+    x["k"][1, :, :, 0] = ((pos % 300).float() / 8).to(torch.bfloat16)[:, None]
+    monkeypatch.delenv("GDLA_PREFILL_GRID", raising=False)
+    monkeypatch.delenv("GDLA_PREFILL_RUN_LEN", raising=False)
+    ref = gpu_prefill(x, window, scale=1.0 / 8)
+    assert torch.isfinite(ref.float()).all()
+    for grid in (1, 7, 8, 24):
+        monkeypatch.setenv("GDLA_PREFILL_GRID", str(grid))
+        log("prefill schedule W=%d grid=%d" % (window, grid))
+        assert torch.equal(gpu_prefill(x, window, scale=1.0 / 8), ref), grid
+    monkeypatch.delenv("GDLA_PREFILL_GRID")
+    if 0 < window <= 129:
+        for rl in (1, 2, 5):
+            monkeypatch.setenv("GDLA_PREFILL_RUN_LEN", str(rl))
+            log("prefill schedule W=%d run_len=%d" % (window, rl))
+            assert torch.equal(gpu_prefill(x, window, scale=1.0 / 8), ref), rl
+
+
 def test_sync_check_mode(monkeypatch):
     """GDLA_SYNC_CHECK=1: every call waits for its kernels; results unchanged."""
     monkeypatch.setenv("GDLA_SYNC_CHECK", "1")
