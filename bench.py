@@ -239,10 +239,12 @@ def cpu_info():
     return model, os.cpu_count()
 
 
-def cpu_baseline_headline(x, w, budget_s=15.0):
+def cpu_baseline_headline(x, w, budget_s=15.0, out=None):
     """The fp32 oracle, untuned, on random query rows (all 80 heads) of the
     headline workload's own inputs (copied from the GPU), extrapolated to the
-    whole launch by unmasked (query, key) pairs."""
+    whole launch by unmasked (query, key) pairs.  With the launch's output
+    `out`, the same rows are also compared with it (relative L2 and max abs
+    over the sampled rows, against the fp32 oracle)."""
     import numpy as np
     import torch
     import oracle
@@ -251,15 +253,22 @@ def cpu_baseline_headline(x, w, budget_s=15.0):
     v = x["v"].float().cpu().numpy()
     rng = np.random.default_rng(0)
     n, rows, pairs, sec = 8, 0, 0, 0.0
+    err2 = ref2 = max_abs = 0.0
     while sec < budget_s:
         rt = np.sort(rng.integers(0, w.T, size=n)).astype(np.int32)
         rb = np.zeros(n, np.int32)
         idx = torch.as_tensor(rt, device=x["k"].device).long()
         q = {key: x[key][0, idx].float().cpu().numpy() for key in ("q_signal", "q_noise", "lam", "gate")}
         t0 = time.perf_counter()
-        oracle.prefill_rows(k, v, q["q_signal"], q["q_noise"], q["lam"], q["gate"], rb, rt, window=w.window,
-                            lib=lib)
+        want = oracle.prefill_rows(k, v, q["q_signal"], q["q_noise"], q["lam"], q["gate"], rb, rt,
+                                   window=w.window, lib=lib)
         sec += time.perf_counter() - t0
+        if out is not None:
+            got = out[0, idx].double().cpu().numpy()
+            d = got - np.asarray(want, np.float64)
+            err2 += float((d * d).sum())
+            ref2 += float((np.asarray(want, np.float64) ** 2).sum())
+            max_abs = max(max_abs, float(np.abs(d).max()))
         rows += n
         vis = rt.astype(np.int64) + 1
         if w.window > 0:
@@ -269,12 +278,66 @@ def cpu_baseline_headline(x, w, budget_s=15.0):
     tflops = pairs * N_HEADS * FLOP_PER_PAIR / sec / 1e12
     total = pairs_prefill(w.B, w.T, w.window) * N_HEADS * FLOP_PER_PAIR
     model, ncpu = cpu_info()
-    return {"value": tflops, "unit": "TFLOP/s", "cores": oracle.num_threads(lib), "kind": "oracle",
-            "arithmetic": "fp32 (the oracle's source built with fp32 sums and expf)",
-            "sample": "%d random query rows (all 80 heads) of the %s workload, %.1f s of compute; "
-                      "extrapolated to the whole launch by unmasked pairs" % (rows, w.name, sec),
-            "extrapolated_s_per_step": total / (tflops * 1e12),
-            "cpu_model": model, "host_cpus": ncpu}
+    res = {"value": tflops, "unit": "TFLOP/s", "cores": oracle.num_threads(lib), "kind": "oracle",
+           "arithmetic": "fp32 (the oracle's source built with fp32 sums and expf)",
+           "sample": "%d random query rows (all 80 heads) of the %s workload, %.1f s of compute; "
+                     "extrapolated to the whole launch by unmasked pairs" % (rows, w.name, sec),
+           "extrapolated_s_per_step": total / (tflops * 1e12),
+           "cpu_model": model, "host_cpus": ncpu}
+    if out is not None:
+        res["parity"] = {"rows": rows, "rel_l2": (err2 / ref2) ** 0.5 if ref2 > 0 else 0.0, "max_abs": max_abs}
+    return res
+
+
+def git_sha():
+    """The commit, or where the tree is not a git checkout, "src:" and a hash
+    of the library's sources."""
+    try:
+        import subprocess
+        r = subprocess.run(["git", "rev-parse", "--short=12", "HEAD"], cwd=ROOT, capture_output=True, text=True,
+                           timeout=10)
+        if r.returncode == 0 and r.stdout.strip():
+            return r.stdout.strip()
+    except Exception:
+        pass
+    h = hashlib.sha256()
+    for path in sorted(glob.glob(os.path.join(ROOT, "attention_gdla_prefill_amd", "csrc", "*"))):
+        h.update(open(path, "rb").read())
+    return "src:" + h.hexdigest()[:12]
+
+
+class Results:
+    """--results FILE: one JSON record per measured configuration, appended as
+    it finishes (config, seed, time, rates, fractions of peak, host, git SHA,
+    and the sampled parity of the CPU-baseline leg where there is one).  With
+    --resume, configurations already recorded in the file for the same commit
+    are skipped, so an interrupted run can be continued."""
+
+    def __init__(self, path, resume):
+        self.path, self.sha, self.done = path, git_sha(), set()
+        if path and resume and os.path.exists(path):
+            with open(path) as f:
+                for ln in f:
+                    try:
+                        r = json.loads(ln)
+                    except ValueError:
+                        continue
+                    if r.get("git_sha") == self.sha:
+                        self.done.add(r.get("config"))
+
+    def skip(self, name):
+        return name in self.done
+
+    def add(self, name, rec):
+        if not self.path:
+            return
+        model, ncpu = cpu_info()
+        row = {"config": name, "seed": 0, "time_unix": time.time(), "git_sha": self.sha,
+               "host_cpus": ncpu, "cpu_model": model}
+        row.update(rec)
+        with open(self.path, "a") as f:
+            f.write(json.dumps(row) + "\n")
+        self.done.add(name)
 
 
 def cpu_baseline_configs(full=False):
@@ -365,14 +428,14 @@ def bench_prefill(name, steps, warmup, settle_s=0.0, keep_inputs=False):
     kern_ms = sum(ev) / len(ev)
     flops = pairs_prefill(w.B, w.T, w.window, P) * N_HEADS * FLOP_PER_PAIR
     nbytes = prefill_bytes(w.B, w.T, prefix=P)
-    del out
     res = {"wall_ms": wall, "kernel_ms": kern_ms, "kernel_ms_min": min(ev), "kernel_ms_max": max(ev),
            "flops": flops, "bytes": nbytes, "settle": settle,
            "tflops": flops / (kern_ms * 1e-3) / 1e12, "gbs": nbytes / (kern_ms * 1e-3) / 1e9}
     if keep_inputs:
         res["inputs"] = x
+        res["out"] = out
     else:
-        del x
+        del x, out
         torch.cuda.empty_cache()
     return res
 
@@ -559,6 +622,10 @@ def main():
     ap.add_argument("--peaks", action="store_true",
                     help="also time a bf16 8192^3 GEMM (hipBLASLt via torch) and a 1 GiB device "
                          "copy: achievable-rate references, reported under 'peaks'")
+    ap.add_argument("--results", metavar="FILE",
+                    help="append one JSON record per measured configuration to FILE")
+    ap.add_argument("--resume", action="store_true",
+                    help="with --results: skip the configurations FILE already holds for this commit")
     ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/traffic_<workload>.json from two rocprofv3 --pmc runs "
                          "(FETCH_SIZE, WRITE_SIZE) of this script with --copy-probe, then exit")
@@ -585,21 +652,30 @@ def main():
     L.load()          # fails loudly if the HIP library is missing
 
     w = W.WORKLOADS[args.workload]
+    results = Results(args.results, args.resume)
     print("[bench] %s steps=%d warmup=%d settle=%.2fs" % (args.workload, args.steps, args.warmup, args.settle_s),
           file=sys.stderr, flush=True)
     decode_main = args.workload.startswith("dec_")
     cpu = None
     if decode_main:
         main_res = bench_decode(args.workload, args.steps, args.warmup)
+        results.add(args.workload, {"time_ms": main_res["kernel_ms"], "gbs": main_res["gbs"],
+                                    "hbm_frac": main_res["gbs"] / PEAK_HBM_GBS})
     else:
         main_res = bench_prefill(args.workload, args.steps, args.warmup, args.settle_s,
                                  keep_inputs=not args.no_cpu_baseline)
         if not args.no_cpu_baseline:
             print("[bench] cpu baseline (fp32 oracle, sampled rows of %s)" % args.workload, file=sys.stderr,
                   flush=True)
-            cpu = cpu_baseline_headline(main_res["inputs"], w)
-            del main_res["inputs"]
+            cpu = cpu_baseline_headline(main_res["inputs"], w, out=main_res["out"])
+            del main_res["inputs"], main_res["out"]
             torch.cuda.empty_cache()
+        results.add(args.workload, {
+            "time_ms": main_res["kernel_ms"], "tflops": main_res["tflops"], "gbs": main_res["gbs"],
+            "mfma_frac": main_res["tflops"] / PEAK_BF16_TFLOPS, "hbm_frac": main_res["gbs"] / PEAK_HBM_GBS,
+            "oracle_s_per_step": cpu["extrapolated_s_per_step"] if cpu else None,
+            "rel_l2": cpu["parity"]["rel_l2"] if cpu and "parity" in cpu else None,
+            "max_abs": cpu["parity"]["max_abs"] if cpu and "parity" in cpu else None})
 
     if args.copy_probe:
         a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
@@ -612,10 +688,12 @@ def main():
     if not args.no_decode and not decode_main:
         print("[bench] decode roofline dec_full", file=sys.stderr, flush=True)
         dec_roof = decode_roofline(bench_decode("dec_full", 10, 2), "dec_full")
+        results.add("dec_full", {"time_ms": dec_roof["kernel_ms"], "gbs": dec_roof["achieved"],
+                                 "hbm_frac": dec_roof["frac"]})
 
     extra = {}
     for name in ("pf_full_4k", "pf_swa_32k", "pf_full_128k", "pf_prefix_4k_32k", "pf_swa_rank"):
-        if name == args.workload or name not in wanted:
+        if name == args.workload or name not in wanted or results.skip(name):
             continue
         print("[bench] extra %s" % name, file=sys.stderr, flush=True)
         steps, warm = (3, 1) if name == "pf_full_128k" else (50, 10)
@@ -623,22 +701,30 @@ def main():
         extra[name] = {"tflops": r["tflops"], "mfma_frac": r["tflops"] / PEAK_BF16_TFLOPS,
                        "gbs": r["gbs"], "hbm_frac": r["gbs"] / PEAK_HBM_GBS, "kernel_ms": r["kernel_ms"],
                        "steps": steps, "settle": r["settle"], "traffic": load_traffic(name)}
+        results.add(name, {"time_ms": r["kernel_ms"], "tflops": r["tflops"], "gbs": r["gbs"],
+                           "mfma_frac": extra[name]["mfma_frac"], "hbm_frac": extra[name]["hbm_frac"]})
     for name in ("dec_swa", "dec_latent_full", "dec_latent_swa"):
-        if name == args.workload or name not in wanted:
+        if name == args.workload or name not in wanted or results.skip(name):
             continue
         print("[bench] extra %s" % name, file=sys.stderr, flush=True)
         fn = bench_decode_latent if name.startswith("dec_latent") else bench_decode
         extra[name] = fn(name, 10, 2)
         if name == "dec_swa":
             extra[name]["traffic"] = load_traffic(name)
+        results.add(name, {"time_ms": extra[name]["kernel_ms"], "gbs": extra[name]["gbs"],
+                           "hbm_frac": extra[name]["hbm_frac"]})
     for name, shape in (("prep_4k", "pf_full_4k"), ("prep_swa_32k", "pf_swa_32k")):
-        if name not in wanted:
+        if name not in wanted or results.skip(name):
             continue
         print("[bench] extra %s" % name, file=sys.stderr, flush=True)
         extra[name] = dict(bench_prep(shape, 20, 5), shapes=shape)
-    if "bwd_4k" in wanted:
+        results.add(name, {"time_ms": extra[name]["kernel_ms"], "gbs": extra[name]["gbs"],
+                           "hbm_frac": extra[name]["hbm_frac"]})
+    if "bwd_4k" in wanted and not results.skip("bwd_4k"):
         print("[bench] extra bwd_4k", file=sys.stderr, flush=True)
         extra["bwd_4k"] = dict(bench_backward("pf_full_4k", 20, 10), shapes="pf_full_4k")
+        results.add("bwd_4k", {"time_ms": extra["bwd_4k"]["ms"], "tflops": extra["bwd_4k"]["tflops"],
+                               "mfma_frac": extra["bwd_4k"]["mfma_frac"]})
 
     peaks = measured_peaks() if args.peaks else None
 

@@ -45,3 +45,25 @@ def test_more_than_one_gpu_is_refused():
                          text=True, timeout=120)
     assert res.returncode == 2
     assert "one GPU" in res.stderr
+
+
+def test_results_log_appends_and_resumes(tmp_path, monkeypatch):
+    """--results: one JSON record per configuration; --resume skips the ones
+    already recorded for the same commit, and only those."""
+    import json
+    path = str(tmp_path / "results.jsonl")
+    monkeypatch.setattr(bench, "git_sha", lambda: "abc")
+    r = bench.Results(path, resume=True)
+    assert not r.skip("pf_full_4k")
+    r.add("pf_full_4k", {"time_ms": 0.37, "mfma_frac": 0.46})
+    r.add("dec_full", {"time_ms": 4.3})
+    rows = [json.loads(x) for x in open(path)]
+    assert [x["config"] for x in rows] == ["pf_full_4k", "dec_full"]
+    assert rows[0]["git_sha"] == "abc" and rows[0]["seed"] == 0 and rows[0]["time_ms"] == 0.37
+    assert "host_cpus" in rows[0] and "cpu_model" in rows[0]
+    again = bench.Results(path, resume=True)
+    assert again.skip("pf_full_4k") and again.skip("dec_full") and not again.skip("pf_swa_32k")
+    assert not bench.Results(path, resume=False).skip("pf_full_4k")
+    monkeypatch.setattr(bench, "git_sha", lambda: "def")           # another commit: nothing is skipped
+    assert not bench.Results(path, resume=True).skip("pf_full_4k")
+    bench.Results(None, resume=False).add("x", {})                 # no file: a no-op
