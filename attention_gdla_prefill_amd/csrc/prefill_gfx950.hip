@@ -146,12 +146,14 @@ __device__ __forceinline__ void lds_barrier() {
 // Work item = (head instance hi = b*n_kv + j, a run of consecutive query
 // tiles).  The kernel is persistent: one workgroup per CU walks a fixed list
 // of items, so that the next item's queries and first K/V tiles load while the
-// current item's epilogue runs.  Items are ranked by cost (full causal: the
-// last query tiles, the heaviest, first) and dealt in snake order -- round r
-// goes to the workgroups in ascending order for even r and descending for odd
-// r.  When the head instances split evenly over the 8 XCDs, the workgroups of
-// one XCD (blockIdx % 8) deal only the items of that XCD's heads, so a head's
-// K/V stays in one L2.
+// current item's epilogue runs.  The list is head by head; within a head the
+// items are ranked by cost (full causal: the last query tiles, the heaviest,
+// first) and the list is dealt in snake order -- round r goes to the
+// workgroups in ascending order for even r and descending for odd r.  When the
+// head instances split evenly over the 8 XCDs, the workgroups of one XCD
+// (blockIdx % 8) deal only the items of that XCD's heads, one head after the
+// other, so the K/V tiles the XCD's workgroups stream at a time are those of
+// one head, shared in that XCD's L2.
 struct WorkList {
     bool by_xcd;
     int xcd, l, n_l, heads, n_items;
@@ -161,7 +163,7 @@ __device__ __forceinline__ bool work_item(const WorkList &w, int round, int n_ru
                                           int &hi, int &qt_first) {
     const int li = round * w.n_l + ((round & 1) ? w.n_l - 1 - w.l : w.l);
     if (li >= w.n_items) return false;
-    const int rank = li / w.heads, m = li % w.heads;
+    const int rank = li % n_runs, m = li / n_runs;
     hi = w.by_xcd ? 8 * m + w.xcd : m;
     qt_first = (causal ? n_runs - 1 - rank : rank) * run_len;
     return true;
