@@ -17,10 +17,13 @@
 //   online softmax in base 2, as in prefill;
 //   V is staged through a wave-private LDS slice, transposed, for O^T += V^T P^T.
 // The 4 waves then merge (log-sum-exp) in LDS.  When a single workgroup
-// covers the whole visible range -- always for a 128-key sliding window --
-// it applies the combine and gate itself; otherwise it writes (m, l, acc)
-// partials and a second kernel merges the splits and applies the epilogue
+// covers the whole visible range it applies the combine and gate itself;
+// otherwise it writes (m, l, acc) partials and a second kernel merges the
+// splits and applies the epilogue
 //   D = H_S - lambda * Repeat_4(H_N),  out = gate * D.
+// A sliding window of up to 128 keys takes its own kernel (decode_window_kernel,
+// below): one workgroup per (sequence, KV head) that requests all of its loads
+// at once.
 #include "gdla_device.h"
 #include "gdla_launch.h"
 
