@@ -38,6 +38,11 @@
  *     on the final store.
  *   - This build supports group = 4, d_qk = 192, d_v = 128 and any
  *     n_kv >= 1; other head shapes return GDLA_ERR_UNSUPPORTED.
+ *   - Two environment variables, read by the prefill entry points at every
+ *     call, exist for testing: GDLA_PREFILL_GRID (a positive integer) caps the
+ *     number of persistent workgroups, GDLA_PREFILL_RUN_LEN sets the query
+ *     tiles per work item of a window of up to 129 keys.  Results do not
+ *     depend on either.
  */
 #ifndef GDLA_H
 #define GDLA_H
