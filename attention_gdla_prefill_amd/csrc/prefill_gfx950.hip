@@ -123,8 +123,26 @@ __device__ __forceinline__ u32x2 bld8(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
 __device__ __forceinline__ void bst16(__amdgpu_buffer_rsrc_t rs, uint32_t off, u32x4 v) {
     __builtin_amdgcn_raw_buffer_store_b128(v, rs, off, 0, 2);
 }
-__device__ __forceinline__ void copy16_to_lds(__amdgpu_buffer_rsrc_t rsrc, uint32_t byte_off, __bf16 *lds_base) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t *)lds_base, 16, byte_off, 0, 0, 0);
+// One 16-byte buffer -> LDS copy per lane: lane l writes lds_addr + 16*l (the
+// LDS address goes to M0).  Written as a statement the compiler does not model
+// as an LDS write: otherwise it waits for every vector memory operation in
+// flight before the next LDS read (the first K read of every slice), which
+// drains the copies issued two tiles ahead and any other load in flight.  The
+// kernel orders the copies against the reads itself: a wait for the wave's
+// older copies and a barrier before a tile is read, and a slot is refilled
+// only after the barrier that ends its last reader.  The nop is the wait state
+// an LDS-DMA load needs after M0 is written.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4 copy_rsrc(const void *base, uint32_t bytes) {
+    const uint64_t a = (uint64_t)(uintptr_t)base;
+    return i32x4{(int)(uint32_t)a, (int)(uint32_t)(a >> 32), (int)bytes, 0x00020000};
+}
+__device__ __forceinline__ void copy16_to_lds(const i32x4 &rsrc, uint32_t byte_off, uint32_t lds_addr) {
+    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                 :: "v"(byte_off), "s"(rsrc), "{m0}"(lds_addr) : "memory");
+}
+__device__ __forceinline__ uint32_t lds_addr_of(const __bf16 *p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) __bf16 *)p;
 }
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 __device__ __forceinline__ s16x4 lds_read_tr16(const __bf16 *p) {
@@ -225,10 +243,12 @@ __device__ __forceinline__ void run(const PrefillParams &p, KRing &kring, VRing 
     // ---- K/V tile copies, HBM -> LDS: wave w issues K copies w, w+8, w+16,
     // w+24 and V copies w, w+8 (and w+16 for w < 6)
     const uint32_t krow_b = (uint32_t)n_kv * D_QK * 2, vrow_b = (uint32_t)n_kv * D_V * 2;
-    __amdgpu_buffer_rsrc_t k_rsrc, v_rsrc;
+    __amdgpu_buffer_rsrc_t k_rsrc;          // the reference pass's global K reads
+    i32x4 kc_rsrc, vc_rsrc;                 // the tile copies
     auto set_rsrc = [&](long s0, int jj) {
         k_rsrc = make_rsrc(p.k + (s0 * n_kv + jj) * D_QK, (uint32_t)T * krow_b);
-        v_rsrc = make_rsrc(p.v + (s0 * n_kv + jj) * D_V, (uint32_t)T * vrow_b);
+        kc_rsrc = copy_rsrc(p.k + (s0 * n_kv + jj) * D_QK, (uint32_t)T * krow_b);
+        vc_rsrc = copy_rsrc(p.v + (s0 * n_kv + jj) * D_V, (uint32_t)T * vrow_b);
     };
     set_rsrc(kseq0, j);
     const int uwave = __builtin_amdgcn_readfirstlane(wave);
@@ -243,13 +263,13 @@ __device__ __forceinline__ void run(const PrefillParams &p, KRing &kring, VRing 
 #pragma unroll
         for (int c = 0; c < K_COPIES_PER_WAVE; ++c) {
             const int row0 = K_ROWS_PER_COPY * (uwave + WAVES * c);
-            if (k_on) copy16_to_lds(k_rsrc, k_lane + (uint32_t)(kbase + row0) * krow_b, ks + row0 * KS_ROW);
+            if (k_on) copy16_to_lds(kc_rsrc, k_lane + (uint32_t)(kbase + row0) * krow_b, lds_addr_of(ks + row0 * KS_ROW));
         }
 #pragma unroll
         for (int c = 0; c < V_COPIES_PER_WAVE; ++c) {
             const int row0 = V_ROWS_PER_COPY * (uwave + WAVES * c);
             if (row0 < BN && v_on && row0 + v_lr < BN)
-                copy16_to_lds(v_rsrc, v_lane + (uint32_t)(kbase + row0) * vrow_b, vs + row0 * VS_ROW);
+                copy16_to_lds(vc_rsrc, v_lane + (uint32_t)(kbase + row0) * vrow_b, lds_addr_of(vs + row0 * VS_ROW));
         }
     };
     // Wait for this wave's copies of all but its newest tile (which may stay
