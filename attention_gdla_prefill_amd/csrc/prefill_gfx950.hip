@@ -42,7 +42,7 @@
 // accumulators alone take 280 of its 512 registers) has to interleave both
 // itself, and the softmax of a slice's second key block waits on nothing but
 // the products that follow it: that layout measured 433 ms at T = 131072
-// against 365 ms for this one.  Each wave needs at most 256 registers, so two
+// against 365 ms for this one when it came in (on the same box).  Each wave needs at most 256 registers, so two
 // fit on a SIMD.  In the epilogue wave A hands the normalised noise-head
 // output H_N of its 16 tokens to wave B through LDS (lane to lane: both waves
 // hold the same tokens and columns in the same lanes), in two halves of 64

@@ -90,11 +90,39 @@ def traffic_kernels(workload):
     return ("prefill_kernel",)
 
 
+def strip_comments(src):
+    """C/C++ source without its comments and blank space: // and /* */
+    comments outside string and character literals are dropped, and every run
+    of white space becomes one blank."""
+    out, i, n = [], 0, len(src)
+    while i < n:
+        c = src[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and src[j] != c:
+                j += 2 if src[j] == "\\" else 1
+            out.append(src[i:j + 1])
+            i = j + 1
+        elif src.startswith("//", i):
+            j = src.find("\n", i)
+            i = n if j < 0 else j
+        elif src.startswith("/*", i):
+            j = src.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def source_hash(kind="prefill"):
-    """Hash of the files a workload's kernels are built from."""
+    """Hash of the code (comments and spacing aside) of the files a workload's
+    kernels are built from."""
     h = hashlib.sha256()
     for name in TRAFFIC_SOURCES[kind]:
-        h.update(open(os.path.join(ROOT, "attention_gdla_prefill_amd", "csrc", name), "rb").read())
+        src = open(os.path.join(ROOT, "attention_gdla_prefill_amd", "csrc", name), encoding="utf-8").read()
+        h.update(strip_comments(src).encode())
     return h.hexdigest()[:16]
 
 

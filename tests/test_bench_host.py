@@ -67,3 +67,21 @@ def test_results_log_appends_and_resumes(tmp_path, monkeypatch):
     monkeypatch.setattr(bench, "git_sha", lambda: "def")           # another commit: nothing is skipped
     assert not bench.Results(path, resume=True).skip("pf_full_4k")
     bench.Results(None, resume=False).add("x", {})                 # no file: a no-op
+
+
+def test_traffic_records_survive_comment_edits(tmp_path, monkeypatch):
+    """A traffic record holds while the kernels' code is unchanged: the source
+    hash ignores comments and spacing, and changes with the code."""
+    import shutil
+    src = os.path.join(ROOT, "attention_gdla_prefill_amd", "csrc")
+    dst = tmp_path / "attention_gdla_prefill_amd" / "csrc"
+    shutil.copytree(src, dst, ignore=shutil.ignore_patterns("*.o", "*.so"))
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    h0 = bench.source_hash("prefill")
+    f = dst / "prefill_gfx950.hip"
+    text = f.read_text()
+    f.write_text("// a new first line\n" + text.replace("namespace gdla {", "namespace gdla {  /* x */\n\n", 1))
+    assert bench.source_hash("prefill") == h0
+    f.write_text(text.replace("constexpr int BM = 64;", "constexpr int BM = 32;", 1))
+    assert bench.source_hash("prefill") != h0
+    assert bench.strip_comments('a = "//"; // c\nb = 1; /* d */ c') == 'a = "//"; b = 1; c'
