@@ -33,6 +33,7 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
+PEAK_CLOCK_MHZ = 2400.0          # the clock the published dense peaks assume
 METRIC = "GDLA prefill TFLOP/s + decode HBM GB/s, each as % of MI355X roofline"
 PEAK_BF16_TFLOPS = 2516.6      # 256 CU x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU
 PEAK_HBM_GBS = 8000.0
@@ -191,10 +192,62 @@ def load_traffic(name):
     return t.get("bytes_per_launch")
 
 
-def time_kernel(fn, steps, warmup, stream, settle_s=0.0):
+class ClockSampler:
+    """Samples the GPU's graphics clock (mean over its XCDs) and socket power
+    every 50 ms through amdsmi while running; all None where amdsmi is not
+    usable.  Informational: the rooflines are priced at the published peaks."""
+
+    def __init__(self, period_s=0.05):
+        self.period, self.clk, self.power, self._stop, self._th = period_s, [], [], None, None
+
+    def _read(self, amdsmi, h):
+        m = amdsmi.amdsmi_get_gpu_metrics_info(h)
+        clks = [c for c in (m.get("current_gfxclks") or []) if isinstance(c, (int, float)) and c > 0]
+        if clks:
+            self.clk.append(sum(clks) / len(clks))
+        pw = m.get("current_socket_power")
+        if isinstance(pw, (int, float)):
+            self.power.append(pw)
+
+    def start(self):
+        import threading
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            h = amdsmi.amdsmi_get_processor_handles()[0]
+        except Exception:
+            return self
+        self._stop = threading.Event()
+
+        def loop():
+            try:
+                while not self._stop.is_set():
+                    self._read(amdsmi, h)
+                    self._stop.wait(self.period)
+            except Exception:
+                pass
+            finally:
+                try:
+                    amdsmi.amdsmi_shut_down()
+                except Exception:
+                    pass
+        self._th = threading.Thread(target=loop, daemon=True)
+        self._th.start()
+        return self
+
+    def stop(self):
+        if self._th is not None:
+            self._stop.set()
+            self._th.join(timeout=5)
+        mean = lambda v: sum(v) / len(v) if v else None
+        return {"gfx_clock_mhz": mean(self.clk), "socket_power_w": mean(self.power), "samples": len(self.clk)}
+
+
+def time_kernel(fn, steps, warmup, stream, settle_s=0.0, sampler=None):
     """Run fn untimed until at least `warmup` launches and `settle_s` seconds
-    of steady work have passed, then `steps` timed launches.  Returns (wall
-    ms/step, per-launch HIP-event ms list, settle record)."""
+    of steady work have passed, then `steps` timed launches (with `sampler`
+    running over them, if given).  Returns (wall ms/step, per-launch HIP-event
+    ms list, settle record)."""
     import torch
     t0 = time.perf_counter()
     n = 0
@@ -207,6 +260,8 @@ def time_kernel(fn, steps, warmup, stream, settle_s=0.0):
     settle = {"launches": n, "seconds": round(time.perf_counter() - t0, 3)}
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(steps)]
+    if sampler is not None:
+        sampler.start()
     t0 = time.perf_counter()
     for a, b in ev:
         a.record(stream)
@@ -214,6 +269,8 @@ def time_kernel(fn, steps, warmup, stream, settle_s=0.0):
         b.record(stream)
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) * 1e3 / steps
+    if sampler is not None:
+        settle = dict(settle, clock=sampler.stop())
     return wall, [a.elapsed_time(b) for a, b in ev], settle
 
 
@@ -434,7 +491,7 @@ def cpu_baseline_configs(full=False):
     return res
 
 
-def bench_prefill(name, steps, warmup, settle_s=0.0, keep_inputs=False):
+def bench_prefill(name, steps, warmup, settle_s=0.0, keep_inputs=False, sample_clock=False):
     import torch
     import attention_gdla_prefill_amd as gdla
     import workload as W
@@ -452,7 +509,8 @@ def bench_prefill(name, steps, warmup, settle_s=0.0, keep_inputs=False):
         out = torch.empty((w.B, w.T - P, w.n_sig, 128), dtype=torch.bfloat16, device="cuda")
         fn = lambda: gdla.prefill_prefix(x["q_signal"], x["q_noise"], x["k"], x["v"], x["lam"],
                                          x["gate"], window=w.window, out=out)
-    wall, ev, settle = time_kernel(fn, steps, warmup, stream, settle_s)
+    wall, ev, settle = time_kernel(fn, steps, warmup, stream, settle_s,
+                                   sampler=ClockSampler() if sample_clock else None)
     kern_ms = sum(ev) / len(ev)
     flops = pairs_prefill(w.B, w.T, w.window, P) * N_HEADS * FLOP_PER_PAIR
     nbytes = prefill_bytes(w.B, w.T, prefix=P)
@@ -691,7 +749,7 @@ def main():
                                     "hbm_frac": main_res["gbs"] / PEAK_HBM_GBS})
     else:
         main_res = bench_prefill(args.workload, args.steps, args.warmup, args.settle_s,
-                                 keep_inputs=not args.no_cpu_baseline)
+                                 keep_inputs=not args.no_cpu_baseline, sample_clock=True)
         if not args.no_cpu_baseline:
             print("[bench] cpu baseline (fp32 oracle, sampled rows of %s)" % args.workload, file=sys.stderr,
                   flush=True)
@@ -787,6 +845,12 @@ def main():
                 "kernel_ms_max": main_res["kernel_ms_max"], "flops_per_launch": main_res["flops"],
                 "algorithmic_bytes_per_launch": main_res["bytes"],
                 "hbm_frac_algorithmic": main_res["gbs"] / PEAK_HBM_GBS}
+        clk = (main_res.get("settle") or {}).get("clock") or {}
+        if clk.get("gfx_clock_mhz"):
+            # the published peak assumes 2.4 GHz; the same kernel's share of
+            # the peak at the clock the box held over the timed launches
+            roof["gfx_clock_mhz"] = clk["gfx_clock_mhz"]
+            roof["frac_at_measured_clock"] = roof["frac"] * PEAK_CLOCK_MHZ / clk["gfx_clock_mhz"]
         config = {"workload": "%s: prefill B=%d T=%d, %d KV / %d signal / %d noise heads, qk 192 / v 128, %s"
                               % (w.name, w.B, w.T, w.n_kv, w.n_sig, w.n_kv,
                                  "full causal" if w.window == 0 else "window %d" % w.window),
