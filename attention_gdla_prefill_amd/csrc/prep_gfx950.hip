@@ -19,7 +19,9 @@
 // Blocks of PP_TOK = 16 consecutive tokens (of the flattened [B*T]), 4 waves
 // per workgroup.  The step moves ~62 KB per token and does ~0.5 MFLOP of
 // lambda per token, so it is bound by HBM; lambda runs on MFMA so that its
-// 4096-long dot products stay off the critical path.
+// 4096-long dot products stay off the critical path, and from LAM_WIDE_MIN_TOK
+// tokens on it stages W^lambda in LDS for 64 tokens at a time, which keeps its
+// re-reads of W^lambda from the L2 below those of x from HBM.
 #include "gdla_device.h"
 #include "gdla_launch.h"
 
@@ -35,16 +37,29 @@ struct PrepParams {
     const __bf16 *k_rope, *x, *w_lambda, *gate_pre;
     __bf16 *lam, *gate;
     long n_tok;                           // B * T
+    int lam_wide;                         // lambda by LAM_TOK-token workgroups (else 16-token ones)
     int T, n_kv, d_model, pos0;
     double theta;
 };
 
 // Workgroup (16-token block, job): job 0 = lambda, job 1 = rotary
 // embedding, jobs 2 .. 1+PP_GATE_PARTS = one part each of the gate, so that
-// the memory streams of a block run side by side on different CUs.
+// the memory streams of a block run side by side on different CUs.  In the
+// wide form of lambda, job-0 workgroup x takes tokens 64x .. 64x+63, and those
+// past the end return at once.
 constexpr int PP_GATE_PARTS = 4;
 constexpr int PP_JOBS = 2 + PP_GATE_PARTS;
 constexpr int PP_HB = 4;              // head blocks of 16 per lambda pass (64 heads)
+constexpr int LAM_TOK = 64;           // tokens per lambda workgroup (16 per wave)
+constexpr int LAM_KC = 64;            // d_model values per staged W^lambda chunk
+constexpr int LAM_ROW = 2 * LAM_KC + 16;  // LDS bytes per head row of a chunk (16 padding)
+constexpr int LAM_BUF = 64 * LAM_ROW;     // one chunk for 64 heads
+// From this many tokens on, lambda takes the wide form: it then has enough
+// workgroups to fill the chip, and it reads W^lambda a quarter as often.
+// Below it, the 16-token form's four times as many workgroups finish sooner.
+constexpr long LAM_WIDE_MIN_TOK = 8192;
+static_assert(2 * LAM_BUF >= (int)sizeof(float2) * PP_TOK * PP_PAIRS, "LDS union too small");
+static_assert(2 * LAM_BUF >= (int)sizeof(float) * 4 * PP_TOK * PP_HB * 16, "LDS union too small");
 constexpr int PP_BATCH = 4;           // rotary tasks / gate chunks per thread in flight
 
 __device__ __forceinline__ uint32_t rotate_pair(uint32_t w, float2 c) {
@@ -53,14 +68,16 @@ __device__ __forceinline__ uint32_t rotate_pair(uint32_t w, float2 c) {
 }
 
 __global__ __launch_bounds__(PP_THREADS) void prep_kernel(PrepParams p) {
-    __shared__ float2 cs[PP_TOK][PP_PAIRS];     // (cos, sin) of every (token, pair)
-    __shared__ float red[4][PP_TOK][PP_HB * 16]; // lambda partial sums of the 4 waves
+    // lambda's two W^lambda chunks, or (cos, sin) of every (token, pair) of the block
+    __shared__ __align__(16) unsigned char smem[2 * LAM_BUF];
+    float2 (*cs)[PP_PAIRS] = reinterpret_cast<float2 (*)[PP_PAIRS]>(smem);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, job = blockIdx.y;
     const long tok0 = (long)blockIdx.x * PP_TOK;
     const int n_tok_blk = (int)min((long)PP_TOK, p.n_tok - tok0);
     const int n_sig = p.n_kv * GROUP, n_qh = n_sig + p.n_kv;
 
-    if (job == 0) {
+    if (job == 0 && !p.lam_wide) {
+        float (*red)[PP_TOK][PP_HB * 16] = reinterpret_cast<float (*)[PP_TOK][PP_HB * 16]>(smem);
         // ---- lambda = sigmoid(x W^lambda^T).  Wave w takes a quarter of the
         // d_model/32 steps for 64 heads at a time (4 MFMA chains).  A = x rows
         // (lane (r, g): token r, values 8g..8g+7 of a 32-value step), B =
@@ -114,6 +131,87 @@ __global__ __launch_bounds__(PP_THREADS) void prep_kernel(PrepParams p) {
                 }
             }
             __syncthreads();
+        }
+    } else if (job == 0) {
+        // ---- lambda = sigmoid(x W^lambda^T) for LAM_TOK tokens: wave w owns
+        // tokens 16w..16w+15 and 64 heads at a time (4 MFMA chains).  The
+        // W^lambda chunk of LAM_KC values is staged in LDS once for the 4
+        // waves (double-buffered; loads run two chunks ahead of the products,
+        // x rows three), so W^lambda is read once per LAM_TOK tokens.  A = x
+        // rows (lane (r, g): token r, values 8g..8g+7 of a 32-value step), B =
+        // W^lambda rows from LDS (lane (r, g): head r, the same values).
+        const long lt0 = (long)blockIdx.x * LAM_TOK;
+        if (lt0 >= p.n_tok) return;
+        const int r = lane & 15, g = lane >> 4;
+        const long tok = lt0 + 16 * wave + r;
+        const bool t_ok = tok < p.n_tok;
+        const __bf16 *xa = p.x + (t_ok ? tok : 0) * p.d_model + 8 * g;
+        const int n_ch = (p.d_model + LAM_KC - 1) / LAM_KC;
+        const u32x4 z = {0, 0, 0, 0};
+        for (int h0 = 0; h0 < n_sig; h0 += 64) {
+            // this thread's share of a W^lambda chunk: 16-byte pieces tid and tid + 256
+            auto load_w = [&](int c, u32x4 (&w)[2]) {
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    const int i = tid + PP_THREADS * u, hh = i >> 3, k = c * LAM_KC + 8 * (i & 7);
+                    w[u] = (c < n_ch && h0 + hh < n_sig && k < p.d_model)
+                               ? ldg16(p.w_lambda + (long)(h0 + hh) * p.d_model + k) : z;
+                }
+            };
+            auto store_w = [&](int c, const u32x4 (&w)[2]) {
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    const int i = tid + PP_THREADS * u;
+                    *reinterpret_cast<u32x4 *>(smem + (c & 1) * LAM_BUF + (i >> 3) * LAM_ROW + 16 * (i & 7)) = w[u];
+                }
+            };
+            auto load_x = [&](int c, u32x4 (&a)[2]) {
+#pragma unroll
+                for (int s = 0; s < 2; ++s) {
+                    const int k = c * LAM_KC + 32 * s;
+                    a[s] = (t_ok && c < n_ch && k < p.d_model) ? ldg16(xa + k) : z;
+                }
+            };
+            f32x4 acc[4];
+#pragma unroll
+            for (int hb = 0; hb < 4; ++hb) acc[hb] = f32x4{0.f, 0.f, 0.f, 0.f};
+            u32x4 wn[2], w2[2], xc[2], xn[2], x2[2];
+            load_w(0, wn);
+            load_x(0, xc);
+            load_x(1, xn);
+            store_w(0, wn);
+            load_w(1, wn);
+            __syncthreads();
+            for (int c = 0; c < n_ch; ++c) {
+                load_w(c + 2, w2);
+                load_x(c + 2, x2);
+                const unsigned char *buf = smem + (c & 1) * LAM_BUF;
+#pragma unroll
+                for (int s = 0; s < 2; ++s)
+#pragma unroll
+                    for (int hb = 0; hb < 4; ++hb) {
+                        const u32x4 b = *reinterpret_cast<const u32x4 *>(buf + (16 * hb + r) * LAM_ROW + 64 * s + 16 * g);
+                        acc[hb] = mfma16(__builtin_bit_cast(bf16x8, xc[s]), __builtin_bit_cast(bf16x8, b), acc[hb]);
+                    }
+                store_w(c + 1, wn);
+                __syncthreads();
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    wn[u] = w2[u];
+                    xc[u] = xn[u];
+                    xn[u] = x2[u];
+                }
+            }
+            // lane (r, g) holds tokens 4g..4g+3 (of the wave's 16) of head h0 + 16hb + r
+#pragma unroll
+            for (int hb = 0; hb < 4; ++hb)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const long t = lt0 + 16 * wave + 4 * g + e;
+                    const int h = h0 + 16 * hb + r;
+                    if (t < p.n_tok && h < n_sig)
+                        p.lam[t * n_sig + h] = (__bf16)(1.f / (1.f + __expf(-acc[hb][e])));
+                }
         }
     } else if (job == 1) {
         // ---- angles: fp64 from position and frequency to sine and cosine (a
@@ -215,6 +313,7 @@ hipError_t launch_prep(void *q_signal, void *q_noise, const void *k_rope, void *
     p.d_model = d_model;
     p.pos0 = pos0;
     p.theta = (double)rope_theta;
+    p.lam_wide = p.n_tok >= LAM_WIDE_MIN_TOK;
     hipLaunchKernelGGL(prep_kernel, dim3((unsigned)prep_grid_blocks(p.n_tok), PP_JOBS), dim3(PP_THREADS), 0, stream, p);
     return hipGetLastError();
 }

@@ -614,8 +614,16 @@ def assert_bf16_close(got, want, what, rel=2.0 ** -7, abs_=1e-6):
     assert np.all(err <= bound), "%s: %d elements outside the bf16 bound" % (what, int(np.sum(err > bound)))
 
 
-def check_prep(got, d, pos0, theta=10000.0):
+def check_prep(got, d, pos0, theta=10000.0, rows=None):
+    """rows = (b, t0, t1): compare sequence b's tokens t0 .. t1-1 only (each
+    token's results depend on its own inputs and its position alone)."""
     import oracle
+    if rows is not None:
+        b, t0, t1 = rows
+        cut = lambda t: t[b:b + 1, t0:t1]
+        got = {k: cut(v) for k, v in got.items()}
+        d = {k: (v if k == "w_lambda" else cut(v)) for k, v in d.items()}
+        pos0 = pos0 + t0
     f = lambda t: t.detach().float().cpu().numpy()
     want = oracle.prep(f(d["q_signal"]), f(d["q_noise"]), f(d["k_rope"]), f(d["x"]), f(d["w_lambda"]),
                        f(d["gate_pre"]), pos0=pos0, theta=theta)
@@ -633,8 +641,11 @@ def check_prep(got, d, pos0, theta=10000.0):
 
 PREP_CASES = [
     # (B, T, n_kv, d_model, pos0): one full head group at the hidden size; odd
-    # shapes; positions near the 256K context
+    # shapes; positions near the 256K context; past 8192 tokens, where lambda
+    # is computed 64 tokens to a workgroup: a ragged last 64 (37 tokens), two
+    # passes over the heads (68), a ragged last chunk of d_model (160 = 2.5 x 64)
     (1, 37, 16, 4096, 0), (2, 20, 3, 96, 1000), (1, 5, 1, 32, 262000), (3, 17, 17, 160, 7),
+    (1, 8229, 17, 160, 5),
 ]
 
 
@@ -662,6 +673,20 @@ def test_prep_config_4k():
     d = W.prep_inputs(w, seed=0, device="cuda")
     check_prep(gpu_prep(d, 0), d, 0)
     del d
+    torch.cuda.empty_cache()
+
+
+def test_prep_config_swa_32k_sampled():
+    """The 32K window prefill's shapes (2 x 32768 tokens, 16 KV heads, hidden
+    size 4096; lambda 64 tokens to a workgroup): token ranges at both ends of
+    each sequence and in the middle, against the oracle on those tokens."""
+    w = W.WORKLOADS["pf_swa_32k"]
+    log("prep at pf_swa_32k shapes, sampled token ranges")
+    d = W.prep_inputs(w, seed=3, device="cuda")
+    got = gpu_prep(d, 0)
+    for rows in ((0, 0, 80), (0, 16381, 16451), (1, 0, 64), (1, 32700, 32768)):
+        check_prep(got, d, 0, rows=rows)
+    del d, got
     torch.cuda.empty_cache()
 
 
