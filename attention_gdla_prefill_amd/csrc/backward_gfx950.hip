@@ -17,15 +17,17 @@
 //
 // Kernels (all deterministic: every output element is summed by one lane):
 //   bwd_pre_kernel   the element-wise differential/gate part, dH and delta;
-//   bwd_dkdv_kernel  per (sequence, KV head, 128-key block): wave w of 8 owns
-//                    16 keys and walks every query tile that sees them for all
+//   bwd_dkdv_kernel  per (sequence, KV head, 128-key block): wave w of 4 owns
+//                    32 keys and walks every query tile that sees them for all
 //                    5 heads;
 //   bwd_dq_kernel    per (sequence, KV head, 128-query tile): wave w of 8 owns
 //                    16 queries and walks every key block they see, head by
 //                    head.
-// Two waves per SIMD (at most 256 registers each): while one wave waits on an
-// LDS read or its exponentials, the other's products keep the matrix core
-// busy, and every 64-row tile in LDS serves eight waves.
+// dK/dV: one wave per SIMD with 512 registers, which hold the K and V
+// fragments and the dK and dV sums of 32 keys, so each fragment read from LDS
+// serves two products.  dQ: two waves per SIMD (at most 256 registers each):
+// while one wave waits on an LDS read or its exponentials, the other's
+// products keep the matrix core busy.
 // Products are bf16 MFMA (16x16x32) with fp32 accumulation; operands that
 // have to be transposed come from LDS through the transposing reads.
 #include "gdla_device.h"
@@ -35,7 +37,7 @@ namespace gdla {
 
 constexpr int BW_T = 64;                   // query tile and key block
 constexpr int BW_THREADS = 256;            // element-wise kernel
-constexpr int BW_GW = 8;                   // waves of a gradient workgroup (two per SIMD)
+constexpr int BW_GW = 8;                   // waves of a dQ workgroup (two per SIMD)
 constexpr int BW_GRAD_THREADS = 64 * BW_GW;
 constexpr int BW_OWN = 16 * BW_GW;         // keys (dK/dV) or queries (dQ) of a gradient workgroup
 // LDS rows padded by 32 bytes: the 16 rows a fragment read or a transposing
@@ -106,13 +108,13 @@ __device__ __forceinline__ uint32_t bw_lds(const T *p) {
 // pad): each copy instruction covers whole rows (2 rows of 26 chunks for the
 // 192-wide tiles, 3 rows of 18 chunks for the 128-wide ones), so a lane's row
 // and chunk within an instruction are fixed and the pad chunks are skipped;
-// wave w issues instructions w, w+8, ...
-template <int COLS, int RS>
+// wave w of GW issues instructions w, w+GW, ...
+template <int COLS, int RS, int GW>
 struct BwTileCopy {
     static constexpr int CH = RS / 8;                 // 16-byte chunks per LDS row
     static constexpr int ROWS = 64 / CH;              // rows per instruction
     static constexpr int N = (BW_T + ROWS - 1) / ROWS;
-    static constexpr int PER_WAVE = (N + BW_GW - 1) / BW_GW;
+    static constexpr int PER_WAVE = (N + GW - 1) / GW;
     int lr, ch;
     __device__ __forceinline__ void init(int lane) {
         lr = lane / CH;
@@ -122,7 +124,7 @@ struct BwTileCopy {
     __device__ __forceinline__ void issue(const bw_i32x4 &rsrc, uint32_t row_bytes, uint32_t lds_tile, int wave) const {
 #pragma unroll
         for (int c = 0; c < PER_WAVE; ++c) {
-            const int row0 = ROWS * (wave + BW_GW * c);
+            const int row0 = ROWS * (wave + GW * c);
             if (row0 < BW_T && lr < ROWS && ch < COLS / 8 && row0 + lr < BW_T)
                 bw_copy16(rsrc, (uint32_t)(row0 + lr) * row_bytes + 16 * ch, lds_tile + (uint32_t)(row0 * RS * 2));
         }
@@ -215,14 +217,19 @@ __device__ __forceinline__ BwHead bw_head(const BwdParams &p, int b, int j, int 
     return x;
 }
 
-// ---- 2. dK, dV.  Workgroup (KV head j, 128-key block, sequence b); wave w owns
-// keys kb0 + 16w .. +15 (the first query tile of the block sees none of the
-// keys of waves 4..7: their weights there are 0).  Steps: (query tile, head) for every query tile that
-// sees a key of the block and each of the 5 heads; the Q and dH tiles, the
-// log2-sum-exp and delta of a step are copied two steps ahead into a ring of
-// three LDS slots.  In C layout lane (r, g) holds element [query 16qb + 4g + e]
-// [key r] of S, P, dP, dS.
-__global__ __launch_bounds__(BW_GRAD_THREADS, 1) void bwd_dkdv_kernel(BwdParams p) {
+// ---- 2. dK, dV.  Workgroup (KV head j, 128-key block, sequence b), 4 waves,
+// one per SIMD; wave w owns the 32 keys kb0 + 32w .. +31 as two 16-key blocks
+// (the first query tile of the block sees none of the keys of waves 2, 3:
+// their weights there are 0), so each fragment of Q, dH, Q^T or dH^T read
+// from LDS serves two products.  Steps: (query tile, head) for every query
+// tile that sees a key of the block and each of the 5 heads; the Q and dH
+// tiles, the log2-sum-exp and delta of a step are copied two steps ahead into
+// a ring of three LDS slots.  In C layout lane (r, g) holds element [query
+// 16qb + 4g + e][key r] of S, P, dP, dS.
+constexpr int BW_DK_GW = 4;                       // waves of a dK/dV workgroup
+constexpr int BW_DK_THREADS = 64 * BW_DK_GW;
+constexpr int BW_DK_KB = BW_OWN / (16 * BW_DK_GW); // 16-key blocks per wave (2)
+__global__ __launch_bounds__(BW_DK_THREADS, 1) void bwd_dkdv_kernel(BwdParams p) {
     __shared__ __attribute__((aligned(16))) __bf16 Qs[3][BW_T * BW_QROW];
     __shared__ __attribute__((aligned(16))) __bf16 Hs[3][BW_T * BW_VROW];
     __shared__ __attribute__((aligned(16))) float lse_s[3][BW_T], dl_s[3][BW_T];
@@ -231,24 +238,35 @@ __global__ __launch_bounds__(BW_GRAD_THREADS, 1) void bwd_dkdv_kernel(BwdParams 
     const int j = blockIdx.x, kb0 = blockIdx.y * BW_OWN, b = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, r = lane & 15, g = lane >> 4;
     const int n_h = p.n_kv * HEADS, T = p.T;
-    const int key = kb0 + 16 * wave + r;
-    const long kvrow = ((long)b * T + (key < T ? key : 0)) * p.n_kv + j;
-    // B operands K_w^T (lane: K[key r][32kk + 8g ..]) and V_w^T
-    bf16x8 kf[D_QK / 32], vf[D_V / 32];
+    int key[BW_DK_KB];
+    long kvrow[BW_DK_KB];
+#pragma unroll
+    for (int s = 0; s < BW_DK_KB; ++s) {
+        key[s] = kb0 + 16 * (BW_DK_KB * wave + s) + r;
+        kvrow[s] = ((long)b * T + (key[s] < T ? key[s] : 0)) * p.n_kv + j;
+    }
+    // B operands K_w^T (lane: K[key r][32kk + 8g ..]) and V_w^T of both key blocks
+    bf16x8 kf[BW_DK_KB][D_QK / 32], vf[BW_DK_KB][D_V / 32];
     {
         const u32x4 z = {0, 0, 0, 0};
 #pragma unroll
-        for (int kk = 0; kk < D_QK / 32; ++kk)
-            kf[kk] = __builtin_bit_cast(bf16x8, key < T ? ldg16(p.k + kvrow * D_QK + 32 * kk + 8 * g) : z);
+        for (int s = 0; s < BW_DK_KB; ++s) {
 #pragma unroll
-        for (int kk = 0; kk < D_V / 32; ++kk)
-            vf[kk] = __builtin_bit_cast(bf16x8, key < T ? ldg16(p.v + kvrow * D_V + 32 * kk + 8 * g) : z);
+            for (int kk = 0; kk < D_QK / 32; ++kk)
+                kf[s][kk] = __builtin_bit_cast(bf16x8, key[s] < T ? ldg16(p.k + kvrow[s] * D_QK + 32 * kk + 8 * g) : z);
+#pragma unroll
+            for (int kk = 0; kk < D_V / 32; ++kk)
+                vf[s][kk] = __builtin_bit_cast(bf16x8, key[s] < T ? ldg16(p.v + kvrow[s] * D_V + 32 * kk + 8 * g) : z);
+        }
     }
-    f32x4 dv[D_V / 16], dk[D_QK / 16];
+    f32x4 dv[BW_DK_KB][D_V / 16], dk[BW_DK_KB][D_QK / 16];
 #pragma unroll
-    for (int i = 0; i < D_V / 16; ++i) dv[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < BW_DK_KB; ++s) {
 #pragma unroll
-    for (int i = 0; i < D_QK / 16; ++i) dk[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int i = 0; i < D_V / 16; ++i) dv[s][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < D_QK / 16; ++i) dk[s][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
     const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
 
     // query tiles that see a key of this block
@@ -256,8 +274,8 @@ __global__ __launch_bounds__(BW_GRAD_THREADS, 1) void bwd_dkdv_kernel(BwdParams 
     int qt_hi = (T - 1) / BW_T;
     if (p.window > 0) qt_hi = min(qt_hi, (kb0 + BW_OWN - 1 + p.window - 1) / BW_T);
     const int n_steps = (qt_hi - qt_lo + 1) * HEADS;
-    BwTileCopy<D_QK, BW_QROW> cq;
-    BwTileCopy<D_V, BW_VROW> ch;
+    BwTileCopy<D_QK, BW_QROW, BW_DK_GW> cq;
+    BwTileCopy<D_V, BW_VROW, BW_DK_GW> ch;
     cq.init(lane);
     ch.init(lane);
     const int uwave = __builtin_amdgcn_readfirstlane(wave);
@@ -282,59 +300,84 @@ __global__ __launch_bounds__(BW_GRAD_THREADS, 1) void bwd_dkdv_kernel(BwdParams 
         const int buf = it % 3, q0 = (qt_lo + it / HEADS) * BW_T;
         const __bf16 *qs_ = Qs[buf], *hs_ = Hs[buf];
         // Two halves of 32 queries (16-query blocks 2i, 2i+1): S = Q K_w^T and
-        // dP = dH V_w^T, then P and dS packed as B operands over the pair, then
-        // dV^T += dH^T P and dK^T += Q^T dS.  The rows' log2-sum-exp and delta
-        // are read first and the weight is computed for every element, then
-        // selected (no branch per element).  A pair is visible when 0 <= q -
-        // key < window (one unsigned compare); rows past the sequence end need
-        // no test: their Q, dH and delta read as zeros, so they add nothing to
-        // dV or dK whatever their weight.
+        // dP = dH V_w^T for both key blocks from one read of each fragment,
+        // then P and dS packed as B operands over the pair, then dV^T += dH^T P
+        // and dK^T += Q^T dS, each transposed fragment serving both key
+        // blocks.  The rows' log2-sum-exp and delta are read first and the
+        // weight is computed for every element, then selected (no branch per
+        // element).  A pair is visible when 0 <= q - key < window (one unsigned
+        // compare); rows past the sequence end need no test: their Q, dH and
+        // delta read as zeros, so they add nothing to dV or dK whatever their
+        // weight.
         const uint32_t wlim = p.window == 0 ? 0x7fffffffu : (uint32_t)p.window;
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-            uint32_t pw[2][2], sw[2][2];
+            uint32_t pw[BW_DK_KB][2][2], sw[BW_DK_KB][2][2];
 #pragma unroll
             for (int hb = 0; hb < 2; ++hb) {
                 const int qb = 2 * i + hb;
                 const __bf16 *qa = qs_ + (16 * qb + r) * BW_QROW + 8 * g;
                 const __bf16 *ha = hs_ + (16 * qb + r) * BW_VROW + 8 * g;
-                f32x4 sv = zero4, dpv = zero4;
+                f32x4 sv[BW_DK_KB], dpv[BW_DK_KB];
 #pragma unroll
-                for (int kk = 0; kk < D_QK / 32; ++kk)
-                    sv = mfma16(*reinterpret_cast<const bf16x8 *>(qa + 32 * kk), kf[kk], sv);
+                for (int s = 0; s < BW_DK_KB; ++s) sv[s] = dpv[s] = zero4;
 #pragma unroll
-                for (int kk = 0; kk < D_V / 32; ++kk)
-                    dpv = mfma16(*reinterpret_cast<const bf16x8 *>(ha + 32 * kk), vf[kk], dpv);
+                for (int kk = 0; kk < D_QK / 32; ++kk) {
+                    const bf16x8 a = *reinterpret_cast<const bf16x8 *>(qa + 32 * kk);
+#pragma unroll
+                    for (int s = 0; s < BW_DK_KB; ++s) sv[s] = mfma16(a, kf[s][kk], sv[s]);
+                }
+#pragma unroll
+                for (int kk = 0; kk < D_V / 32; ++kk) {
+                    const bf16x8 a = *reinterpret_cast<const bf16x8 *>(ha + 32 * kk);
+#pragma unroll
+                    for (int s = 0; s < BW_DK_KB; ++s) dpv[s] = mfma16(a, vf[s][kk], dpv[s]);
+                }
                 const float4 lse4 = *reinterpret_cast<const float4 *>(&lse_s[buf][16 * qb + 4 * g]);
                 const float4 dl4 = *reinterpret_cast<const float4 *>(&dl_s[buf][16 * qb + 4 * g]);
                 const float ls[4] = {lse4.x, lse4.y, lse4.z, lse4.w};
                 const float dls[4] = {dl4.x, dl4.y, dl4.z, dl4.w};
-                float pv[4], dsv[4];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float x = fast_exp2(fmaf(sv[e], p.scale_log2, -ls[e]));
-                    pv[e] = (uint32_t)(q0 + 16 * qb + 4 * g + e - key) < wlim ? x : 0.f;
-                    dsv[e] = pv[e] * (dpv[e] - dls[e]);
+                for (int s = 0; s < BW_DK_KB; ++s) {
+                    float pv[4], dsv[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float x = fast_exp2(fmaf(sv[s][e], p.scale_log2, -ls[e]));
+                        pv[e] = (uint32_t)(q0 + 16 * qb + 4 * g + e - key[s]) < wlim ? x : 0.f;
+                        dsv[e] = pv[e] * (dpv[s][e] - dls[e]);
+                    }
+                    pw[s][hb][0] = pack_bf16x2(pv[0], pv[1]);
+                    pw[s][hb][1] = pack_bf16x2(pv[2], pv[3]);
+                    sw[s][hb][0] = pack_bf16x2(dsv[0], dsv[1]);
+                    sw[s][hb][1] = pack_bf16x2(dsv[2], dsv[3]);
                 }
-                pw[hb][0] = pack_bf16x2(pv[0], pv[1]);
-                pw[hb][1] = pack_bf16x2(pv[2], pv[3]);
-                sw[hb][0] = pack_bf16x2(dsv[0], dsv[1]);
-                sw[hb][1] = pack_bf16x2(dsv[2], dsv[3]);
             }
-            const bf16x8 pb = __builtin_bit_cast(bf16x8, (u32x4{pw[0][0], pw[0][1], pw[1][0], pw[1][1]}));
-            const bf16x8 sb = __builtin_bit_cast(bf16x8, (u32x4{sw[0][0], sw[0][1], sw[1][0], sw[1][1]}));
+            bf16x8 pb[BW_DK_KB], sb[BW_DK_KB];
 #pragma unroll
-            for (int db = 0; db < D_V / 16; ++db) dv[db] = mfma16(bw_tr_a(hs_, BW_VROW, 32 * i, 16 * db, r, g), pb, dv[db]);
+            for (int s = 0; s < BW_DK_KB; ++s) {
+                pb[s] = __builtin_bit_cast(bf16x8, (u32x4{pw[s][0][0], pw[s][0][1], pw[s][1][0], pw[s][1][1]}));
+                sb[s] = __builtin_bit_cast(bf16x8, (u32x4{sw[s][0][0], sw[s][0][1], sw[s][1][0], sw[s][1][1]}));
+            }
 #pragma unroll
-            for (int db = 0; db < D_QK / 16; ++db) dk[db] = mfma16(bw_tr_a(qs_, BW_QROW, 32 * i, 16 * db, r, g), sb, dk[db]);
+            for (int db = 0; db < D_V / 16; ++db) {
+                const bf16x8 a = bw_tr_a(hs_, BW_VROW, 32 * i, 16 * db, r, g);
+#pragma unroll
+                for (int s = 0; s < BW_DK_KB; ++s) dv[s][db] = mfma16(a, pb[s], dv[s][db]);
+            }
+#pragma unroll
+            for (int db = 0; db < D_QK / 16; ++db) {
+                const bf16x8 a = bw_tr_a(qs_, BW_QROW, 32 * i, 16 * db, r, g);
+#pragma unroll
+                for (int s = 0; s < BW_DK_KB; ++s) dk[s][db] = mfma16(a, sb[s], dk[s][db]);
+            }
         }
         // step it+2 into the slot of step it-1, which every wave finished
         // before the previous barrier; then step it+1 must have landed (only
-        // the copies just issued -- 6 to 8 per wave -- may stay in flight)
+        // the copies just issued -- 13 to 15 per wave -- may stay in flight)
         // before the bare barrier
         if (it + 2 < n_steps) {
             issue(it + 2);
-            __builtin_amdgcn_s_waitcnt(0x0076);   // vmcnt(6) lgkmcnt(0)
+            __builtin_amdgcn_s_waitcnt(0x007D);   // vmcnt(13) lgkmcnt(0)
         } else {
             __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
         }
@@ -343,16 +386,18 @@ __global__ __launch_bounds__(BW_GRAD_THREADS, 1) void bwd_dkdv_kernel(BwdParams 
         asm volatile("" ::: "memory");
     }
     // lane (r, g) holds dV[key r][16db + 4g + e] and dK[key r][16db + 4g + e] / scale
-    if (key < T) {
+#pragma unroll
+    for (int s = 0; s < BW_DK_KB; ++s) {
+        if (key[s] >= T) continue;
 #pragma unroll
         for (int db = 0; db < D_V / 16; ++db)
-            *reinterpret_cast<u32x2 *>(p.dv + kvrow * D_V + 16 * db + 4 * g) =
-                u32x2{pack_bf16x2(dv[db][0], dv[db][1]), pack_bf16x2(dv[db][2], dv[db][3])};
+            *reinterpret_cast<u32x2 *>(p.dv + kvrow[s] * D_V + 16 * db + 4 * g) =
+                u32x2{pack_bf16x2(dv[s][db][0], dv[s][db][1]), pack_bf16x2(dv[s][db][2], dv[s][db][3])};
 #pragma unroll
         for (int db = 0; db < D_QK / 16; ++db)
-            *reinterpret_cast<u32x2 *>(p.dk + kvrow * D_QK + 16 * db + 4 * g) =
-                u32x2{pack_bf16x2(dk[db][0] * p.scale, dk[db][1] * p.scale),
-                      pack_bf16x2(dk[db][2] * p.scale, dk[db][3] * p.scale)};
+            *reinterpret_cast<u32x2 *>(p.dk + kvrow[s] * D_QK + 16 * db + 4 * g) =
+                u32x2{pack_bf16x2(dk[s][db][0] * p.scale, dk[s][db][1] * p.scale),
+                      pack_bf16x2(dk[s][db][2] * p.scale, dk[s][db][3] * p.scale)};
     }
 }
 
@@ -378,8 +423,8 @@ __global__ __launch_bounds__(BW_GRAD_THREADS, 1) void bwd_dq_kernel(BwdParams p)
     const __bf16 *kseq = p.k + ((long)b * T * p.n_kv + j) * D_QK;
     const __bf16 *vseq = p.v + ((long)b * T * p.n_kv + j) * D_V;
     const long kv_qs = (long)p.n_kv * D_QK, kv_vs = (long)p.n_kv * D_V;
-    BwTileCopy<D_QK, BW_QROW> ck;
-    BwTileCopy<D_V, BW_VROW> cv;
+    BwTileCopy<D_QK, BW_QROW, BW_GW> ck;
+    BwTileCopy<D_V, BW_VROW, BW_GW> cv;
     ck.init(lane);
     cv.init(lane);
     const int uwave = __builtin_amdgcn_readfirstlane(wave);
@@ -538,7 +583,7 @@ hipError_t launch_backward(const void *qs, const void *qn, const void *k, const 
     hipLaunchKernelGGL(bwd_pre_kernel, dim3((unsigned)((units + 7) / 8)), dim3(BW_THREADS), 0, stream, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const unsigned n_t = (unsigned)((T + BW_OWN - 1) / BW_OWN);
-    hipLaunchKernelGGL(bwd_dkdv_kernel, dim3(n_kv, n_t, B), dim3(BW_GRAD_THREADS), 0, stream, p);
+    hipLaunchKernelGGL(bwd_dkdv_kernel, dim3(n_kv, n_t, B), dim3(BW_DK_THREADS), 0, stream, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(bwd_dq_kernel, dim3(n_kv, n_t, B), dim3(BW_GRAD_THREADS), 0, stream, p);
     return hipGetLastError();

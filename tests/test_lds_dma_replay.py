@@ -255,24 +255,25 @@ def test_window_decode_copies(n_vis, n_kv):
 
 
 # ---------------------------------------------------------------------------
-# backward: 64-row tiles, 8 waves, rows of 192 or 128 values (+32-byte pad),
-# and one float per lane for the rows' statistics
+# backward: 64-row tiles, rows of 192 or 128 values (+32-byte pad), and one
+# float per lane for the rows' statistics; the dK/dV kernel runs 4 waves (32
+# keys each), the dQ kernel 8 (16 queries each)
 # ---------------------------------------------------------------------------
 
-BW_WAVES = 8
+DKDV_WAVES, DQ_WAVES = 4, 8
 
 
-def backward_tile_writes(cols, rs):
-    """The copies of one 64-row tile by the 8 waves: (writes, copies per wave)."""
+def backward_tile_writes(cols, rs, n_waves):
+    """The copies of one 64-row tile by n_waves waves: (writes, copies per wave)."""
     ch_per_row = rs // 8
     rows = 64 // ch_per_row
     n = (64 + rows - 1) // rows
     writes = []
     per_wave = []
-    for wave in range(BW_WAVES):
+    for wave in range(n_waves):
         k = 0
-        for c in range((n + BW_WAVES - 1) // BW_WAVES):
-            row0 = rows * (wave + BW_WAVES * c)
+        for c in range((n + n_waves - 1) // n_waves):
+            row0 = rows * (wave + n_waves * c)
             if row0 < 64:
                 writes += rows_copy(ch_per_row, rows, cols // 8, row0, 64, 0, rs * 2, 1234)
                 k += 1
@@ -280,19 +281,22 @@ def backward_tile_writes(cols, rs):
     return writes, per_wave
 
 
+@pytest.mark.parametrize("n_waves", [DKDV_WAVES, DQ_WAVES])
 @pytest.mark.parametrize("cols,rs", [(192, 208), (128, 144)])
-def test_backward_tile_copies(cols, rs):
-    writes, _ = backward_tile_writes(cols, rs)
+def test_backward_tile_copies(cols, rs, n_waves):
+    writes, _ = backward_tile_writes(cols, rs, n_waves)
     check_tile(writes, 64, cols // 8, 0, 64 * rs * 2, rs * 2)
 
 
 def test_backward_step_wait_leaves_only_the_newest_step():
-    """At a step's end a wave waits with vmcnt(6): it must have issued at least
-    6 copies for the step just requested, so every older copy has landed."""
-    q = backward_tile_writes(192, 208)[1]
-    v = backward_tile_writes(128, 144)[1]
-    for w in range(BW_WAVES):
-        assert q[w] + v[w] >= 6          # dK/dV: Q and dH tiles (+ statistics on waves 0, 1)
+    """At a step's end a wave waits with vmcnt(13) (dK/dV, 4 waves) or
+    vmcnt(6) (dQ, 8 waves): it must have issued at least that many copies for
+    the step just requested, so every older copy has landed."""
+    for n_waves, wait in ((DKDV_WAVES, 13), (DQ_WAVES, 6)):
+        q = backward_tile_writes(192, 208, n_waves)[1]
+        v = backward_tile_writes(128, 144, n_waves)[1]
+        for w in range(n_waves):
+            assert q[w] + v[w] >= wait, (n_waves, w, q[w], v[w])
 
 
 def test_backward_lds_fits_and_stat_copies():
