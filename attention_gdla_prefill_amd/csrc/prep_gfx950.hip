@@ -136,8 +136,9 @@ __global__ __launch_bounds__(PP_THREADS) void prep_kernel(PrepParams p) {
         // ---- lambda = sigmoid(x W^lambda^T) for LAM_TOK tokens: wave w owns
         // tokens 16w..16w+15 and 64 heads at a time (4 MFMA chains).  The
         // W^lambda chunk of LAM_KC values is staged in LDS once for the 4
-        // waves (double-buffered; loads run two chunks ahead of the products,
-        // x rows three), so W^lambda is read once per LAM_TOK tokens.  A = x
+        // waves (double-buffered; the loads of W^lambda and of the x rows are
+        // requested two chunks ahead of their products), so W^lambda is read
+        // once per LAM_TOK tokens.  A = x
         // rows (lane (r, g): token r, values 8g..8g+7 of a 32-value step), B =
         // W^lambda rows from LDS (lane (r, g): head r, the same values).
         const long lt0 = (long)blockIdx.x * LAM_TOK;
