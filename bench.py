@@ -675,6 +675,8 @@ def bench_decode_latent(name, steps, warmup):
 PREFILL_WORKLOADS = ("pf_full_128k", "pf_full_4k", "pf_swa_32k", "pf_prefix_4k_32k", "pf_swa_rank")
 EXTRA_NAMES = ("pf_full_4k", "pf_swa_32k", "pf_full_128k", "pf_prefix_4k_32k", "pf_swa_rank", "dec_swa",
                "dec_latent_full", "dec_latent_swa", "prep_4k", "prep_swa_32k", "bwd_4k")
+# measured only when named in --extras
+OPT_IN_EXTRAS = ("bwd_swa_32k",)
 
 
 def decode_roofline(r, name):
@@ -702,7 +704,8 @@ def main():
     ap.add_argument("--no-decode", action="store_true", help="skip the full-causal decode roofline")
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--extras", default=",".join(EXTRA_NAMES),
-                    help="comma-separated extra workloads to time (a profile of one workload names just that one)")
+                    help="comma-separated extra workloads to time (a profile of one workload names just that one); "
+                         "also %s, measured only when named" % ", ".join(OPT_IN_EXTRAS))
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run one 1 GiB device copy (reference for HBM counter scaling)")
     ap.add_argument("--peaks", action="store_true",
@@ -725,7 +728,7 @@ def main():
         sys.exit(2)
     wanted = [] if args.no_extra else [x for x in args.extras.split(",") if x]
     for name in wanted:
-        if name not in EXTRA_NAMES:
+        if name not in EXTRA_NAMES + OPT_IN_EXTRAS:
             print("unknown extra workload %r" % name, file=sys.stderr)
             sys.exit(2)
 
@@ -811,6 +814,11 @@ def main():
         extra["bwd_4k"] = dict(bench_backward("pf_full_4k", 20, 10), shapes="pf_full_4k")
         results.add("bwd_4k", {"time_ms": extra["bwd_4k"]["ms"], "tflops": extra["bwd_4k"]["tflops"],
                                "mfma_frac": extra["bwd_4k"]["mfma_frac"]})
+    if "bwd_swa_32k" in wanted and not results.skip("bwd_swa_32k"):
+        print("[bench] extra bwd_swa_32k", file=sys.stderr, flush=True)
+        extra["bwd_swa_32k"] = dict(bench_backward("pf_swa_32k", 10, 3), shapes="pf_swa_32k")
+        results.add("bwd_swa_32k", {"time_ms": extra["bwd_swa_32k"]["ms"], "tflops": extra["bwd_swa_32k"]["tflops"],
+                                    "mfma_frac": extra["bwd_swa_32k"]["mfma_frac"]})
 
     peaks = measured_peaks() if args.peaks else None
 
