@@ -255,20 +255,28 @@ __global__ __launch_bounds__(DC_THREADS) void decode_split_kernel(DecodeParams p
 __global__ __launch_bounds__(D_V) void decode_combine_kernel(DecodeParams p) {
     const int j = blockIdx.x, b = blockIdx.y, c = threadIdx.x;
     const float *base = p.ws + ((long)b * p.n_kv + j) * p.n_split * PART_FLOATS;
-    float A[HEADS], Ls[HEADS];
+    const int ns = p.n_split;
+    // the splits' maxima of the 5 heads (the same words for every thread)
+    float m[HEADS];
 #pragma unroll
-    for (int h = 0; h < HEADS; ++h) {
-        float m = -INFINITY;
-        for (int s = 0; s < p.n_split; ++s) m = fmaxf(m, base[s * PART_FLOATS + h]);
-        float l = 0.f, acc = 0.f;
-        for (int s = 0; s < p.n_split; ++s) {
-            const float *part = base + s * PART_FLOATS;
-            const float f = part[h] == -INFINITY ? 0.f : fast_exp2(part[h] - m);
-            l += f * part[8 + h];
-            acc += f * part[16 + h * D_V + c];
+    for (int h = 0; h < HEADS; ++h) m[h] = -INFINITY;
+    for (int s = 0; s < ns; ++s)
+#pragma unroll
+        for (int h = 0; h < HEADS; ++h) m[h] = fmaxf(m[h], base[s * PART_FLOATS + h]);
+    // then every split's sums and column c of its outputs, four splits' loads
+    // in flight at a time
+    float Ls[HEADS], A[HEADS];
+#pragma unroll
+    for (int h = 0; h < HEADS; ++h) Ls[h] = A[h] = 0.f;
+#pragma unroll 4
+    for (int s = 0; s < ns; ++s) {
+        const float *part = base + s * PART_FLOATS;
+#pragma unroll
+        for (int h = 0; h < HEADS; ++h) {
+            const float f = part[h] == -INFINITY ? 0.f : fast_exp2(part[h] - m[h]);
+            Ls[h] += f * part[8 + h];
+            A[h] += f * part[16 + h * D_V + c];
         }
-        Ls[h] = l;
-        A[h] = acc;
     }
     decode_epilogue(p, b, j, c, load_gate_col(p, b, j, c), A, Ls);
 }
