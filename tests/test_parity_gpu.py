@@ -643,9 +643,10 @@ PREP_CASES = [
     # (B, T, n_kv, d_model, pos0): one full head group at the hidden size; odd
     # shapes; positions near the 256K context; past 8192 tokens, where lambda
     # is computed 64 tokens to a workgroup: a ragged last 64 (37 tokens), two
-    # passes over the heads (68), a ragged last chunk of d_model (160 = 2.5 x 64)
+    # passes over the heads (68), a ragged last chunk of d_model (160 = 2.5 x 64);
+    # 4 heads and half a chunk of d_model (32) over two sequences
     (1, 37, 16, 4096, 0), (2, 20, 3, 96, 1000), (1, 5, 1, 32, 262000), (3, 17, 17, 160, 7),
-    (1, 8229, 17, 160, 5),
+    (1, 8229, 17, 160, 5), (2, 4100, 1, 32, 3),
 ]
 
 
