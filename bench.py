@@ -36,6 +36,7 @@ sys.path.insert(0, ROOT)
 PEAK_CLOCK_MHZ = 2400.0          # the clock the published dense peaks assume
 METRIC = "GDLA prefill TFLOP/s + decode HBM GB/s, each as % of MI355X roofline"
 PEAK_BF16_TFLOPS = 2516.6      # 256 CU x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU
+PEAK_FP32_TFLOPS = 157.3      # fp32 vector arithmetic, dense
 PEAK_HBM_GBS = 8000.0
 FLOP_PER_PAIR = 640            # 2*192 (QK^T) + 2*128 (PV) per (query head, query, key)
 N_HEADS = 80                   # 64 signal + 16 noise query heads
@@ -666,10 +667,21 @@ def bench_decode_latent(name, steps, warmup):
     expanded = decode_bytes(lengths, w.window)
     del d, out, ws
     torch.cuda.empty_cache()
-    return {"kernel_ms": kern_ms, "bytes": nbytes, "gbs": nbytes / (kern_ms * 1e-3) / 1e9,
-            "hbm_frac": nbytes / (kern_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
-            "expanded_equivalent_gbs": expanded / (kern_ms * 1e-3) / 1e9, "cache": COLD,
-            "kernel_ms_dirty_flush": ms_dirty}
+    res = {"kernel_ms": kern_ms, "bytes": nbytes, "gbs": nbytes / (kern_ms * 1e-3) / 1e9,
+           "hbm_frac": nbytes / (kern_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+           "expanded_equivalent_gbs": expanded / (kern_ms * 1e-3) / 1e9, "cache": COLD,
+           "kernel_ms_dirty_flush": ms_dirty}
+    if 1 <= w.window <= 128:
+        # the one-launch window kernel does its weight products on the vector
+        # ALUs: per (sequence, KV head) q~ = W_uk^T q^C for 5 heads (5 x 128 x 512
+        # multiply-adds), o~ = sum_s p_s c_s over the visible rows (5 x rows x
+        # 512) and D = W_uv d~ for 4 heads (4 x 512 x 128); its bound is the fp32
+        # vector peak, beside which the bytes are few
+        rows = sum(min(L, w.window) for L in lengths)
+        flops = 2 * 512 * (w.B * w.n_kv * (5 * 128 + 4 * 128) + rows * w.n_kv * 5)
+        res.update(valu_flops=flops, valu_tflops=flops / (kern_ms * 1e-3) / 1e12,
+                   valu_frac=flops / (kern_ms * 1e-3) / 1e12 / PEAK_FP32_TFLOPS)
+    return res
 
 
 PREFILL_WORKLOADS = ("pf_full_128k", "pf_full_4k", "pf_swa_32k", "pf_prefix_4k_32k", "pf_swa_rank")
