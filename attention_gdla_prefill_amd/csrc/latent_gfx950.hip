@@ -583,8 +583,9 @@ __global__ __launch_bounds__(LT_C) void latent_combine_kernel(LatentParams p) {
 //      8(t%64) .. +7 over rows 32(t/64) .. +31 of the window, the quarters
 //      add up through LDS; then the differential combine in the latent
 //      space, d~ = o~_S / l_S - lambda o~_N / l_N;
-//   4. D = W_uv[j] d~ (thread t: half of the latent values of output column
-//      t % 128), out = gate * D.
+//   4. D = W_uv[j] d~ on the matrix cores (d~ as its bf16 high and low
+//      parts, the rows of W_uv[j] as B fragments straight from memory), out =
+//      gate * D.
 // The row sums are taken over the fp32 weights that enter o~.
 constexpr int LW_KEYS = 128;
 constexpr int LW_THREADS = 256;
@@ -598,7 +599,8 @@ __global__ __launch_bounds__(LW_THREADS, 2) void latent_window_kernel(LatentPara
     __shared__ float red_m[4][16], red_l[4][16];
     __shared__ __attribute__((aligned(16))) float pw_s[HEADS][LW_KEYS];  // weights
     __shared__ __attribute__((aligned(16))) float part[4][HEADS][LT_C];  // per-quarter partial sums
-    __shared__ float dl[GROUP][LT_C];                                    // d~ of the signal heads
+    // d~ of the signal heads as bf16 high and low parts (their sum keeps ~16 bits)
+    __shared__ __attribute__((aligned(16))) __bf16 dlh[GROUP][LT_C], dll[GROUP][LT_C];
 
     const int j = blockIdx.x, b = blockIdx.y;
     const int n_kv = p.n_kv, n_sig = n_kv * GROUP;
@@ -628,8 +630,6 @@ __global__ __launch_bounds__(LW_THREADS, 2) void latent_window_kernel(LatentPara
     }
     const long orow0 = (long)b * n_sig + GROUP * j;     // signal head 4j
     const u32x2 lw = *reinterpret_cast<const u32x2 *>(p.lam + orow0);     // lambda of the 4 signal heads
-    const int oh = tid >> 6, oc = 2 * (tid & 63);       // output: head 4j + oh, columns oc, oc + 1
-    const uint32_t gw = *reinterpret_cast<const uint32_t *>(p.gate + (orow0 + oh) * D_V + oc);
 
     const int start = __builtin_amdgcn_readfirstlane((int)cuv[0]);
     const int L = __builtin_amdgcn_readfirstlane((int)cuv[1]) - start;
@@ -775,36 +775,52 @@ __global__ __launch_bounds__(LW_THREADS, 2) void latent_window_kernel(LatentPara
                            part[3][h][2 * tid + i]) * inv[h];
         const float lam[GROUP] = {bf16_lo(lw[0]), bf16_hi(lw[0]), bf16_lo(lw[1]), bf16_hi(lw[1])};
 #pragma unroll
-        for (int h = 0; h < GROUP; ++h)
-#pragma unroll
-            for (int i = 0; i < 2; ++i) dl[h][2 * tid + i] = fmaf(-lam[h], o[GROUP][i], o[h][i]);
+        for (int h = 0; h < GROUP; ++h) {
+            const float v0 = fmaf(-lam[h], o[GROUP][0], o[h][0]), v1 = fmaf(-lam[h], o[GROUP][1], o[h][1]);
+            const uint32_t hi = pack_bf16x2(v0, v1);
+            *reinterpret_cast<uint32_t *>(&dlh[h][2 * tid]) = hi;
+            *reinterpret_cast<uint32_t *>(&dll[h][2 * tid]) = pack_bf16x2(v0 - bf16_lo(hi), v1 - bf16_hi(hi));
+        }
     }
     __syncthreads();
 
-    // ---- 4. D[h][d] = sum_c W_uv[j][d][c] d~[h][c]: thread (half q2, column d)
-    // sums latent values 256 q2 .. +255; the halves add up through LDS
+    // ---- 4. D = d~ W_uv[j]^T on the matrix cores: M = the 4 signal heads
+    // (rows 4..15 zero), N = 16 output columns per block (wave w: blocks 2w,
+    // 2w+1), K = the 512 latent values; d~ enters as its bf16 high and low parts,
+    // the B fragments are rows of W_uv[j] straight from memory (lane (r, g):
+    // W_uv[j][16nb + r][32kk + 8g .. +7])
     {
-        const int q2 = tid / D_V, d = tid % D_V, c0 = q2 * (LT_C / 2);
-        const __bf16 *w = p.wuv + ((long)j * D_V + d) * LT_C + c0;
-        u32x4 wv[LT_C / 2 / 8];
+        u32x4 wv[2][LT_C / 32];
 #pragma unroll
-        for (int c = 0; c < LT_C / 2 / 8; ++c) wv[c] = ldg16(w + 8 * c);
-        float acc4[GROUP] = {0.f, 0.f, 0.f, 0.f};
+        for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-        for (int c = 0; c < LT_C / 2 / 8; ++c)
+            for (int kk = 0; kk < LT_C / 32; ++kk)
+                wv[nb][kk] = ldg16(p.wuv + ((long)j * D_V + 16 * (2 * wave + nb) + r) * LT_C + 32 * kk + 8 * g);
+        f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+        const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+        for (int kk = 0; kk < LT_C / 32; ++kk) {
+            const u32x4 ah = r < GROUP ? *reinterpret_cast<const u32x4 *>(&dlh[r < GROUP ? r : 0][32 * kk + 8 * g]) : z;
+            const u32x4 al = r < GROUP ? *reinterpret_cast<const u32x4 *>(&dll[r < GROUP ? r : 0][32 * kk + 8 * g]) : z;
 #pragma unroll
-                for (int h = 0; h < GROUP; ++h) {
-                    acc4[h] = fmaf(bf16_lo(wv[c][i]), dl[h][c0 + 8 * c + 2 * i], acc4[h]);
-                    acc4[h] = fmaf(bf16_hi(wv[c][i]), dl[h][c0 + 8 * c + 2 * i + 1], acc4[h]);
+            for (int nb = 0; nb < 2; ++nb) {
+                const bf16x8 bw = __builtin_bit_cast(bf16x8, wv[nb][kk]);
+                acc[nb] = mfma16(__builtin_bit_cast(bf16x8, ah), bw, acc[nb]);
+                acc[nb] = mfma16(__builtin_bit_cast(bf16x8, al), bw, acc[nb]);
+            }
+        }
+        // lane (r, g): rows 4g..4g+3 (heads; g == 0 holds the 4 signal heads),
+        // column 16 (2w + nb) + r
+        if (g == 0) {
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+                for (int e = 0; e < GROUP; ++e) {
+                    const long o_idx = (orow0 + e) * D_V + 16 * (2 * wave + nb) + r;
+                    p.out[o_idx] = (__bf16)((float)p.gate[o_idx] * acc[nb][e]);
                 }
-#pragma unroll
-        for (int h = 0; h < GROUP; ++h) part[q2][h][d] = acc4[h];
+        }
     }
-    __syncthreads();
-    const float D0 = part[0][oh][oc] + part[1][oh][oc], D1 = part[0][oh][oc + 1] + part[1][oh][oc + 1];
-    *reinterpret_cast<uint32_t *>(p.out + (orow0 + oh) * D_V + oc) = pack_bf16x2(bf16_lo(gw) * D0, bf16_hi(gw) * D1);
 }
 
 int latent_splits(int max_seqlen_k, int window) {
