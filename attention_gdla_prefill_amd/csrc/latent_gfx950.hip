@@ -51,7 +51,7 @@ static_assert(LT_BN / 8 == LT_WAVES && LT_COPIES == LT_BN / LT_WAVES + 1, "copie
 // LDS rows: the c part with a 32-byte pad (conflict-free 16-row fragment reads),
 // the rotary part packed (8 rows per copy instruction)
 constexpr int LT_CS = LT_C + 16;          // bf16 per c row in LDS (1056 bytes)
-constexpr int LT_CHUNK = 4096;            // target keys per workgroup (split)
+constexpr int LT_CHUNK = 8192;            // target keys per workgroup (split)
 
 struct LatentParams {
     const __bf16 *qs, *qn, *lat, *wuk, *wuv, *lam, *gate;
